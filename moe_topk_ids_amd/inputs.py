@@ -1,0 +1,94 @@
+"""Seeded synthetic inputs for the fused MoE forward.
+
+The recipe is the one the atrex-bench operator #009 "fused_moe" page gives
+in its "Input Generation" section, drawn in the same order:
+
+* hidden states: bf16 N(0,1) scaled by 0.1, [T, H];
+* w1: bf16 N(0,1) scaled by H**-0.5, [E, 2I, H] (rows 0..I-1 gate, I..2I-1 up);
+* w2: bf16 N(0,1) scaled by I**-0.5, [E, H, I];
+* router logits: fp32 N(0,1) [T, E]; softmax over experts, the K largest
+  probabilities (distinct experts), renormalised to sum to one; fp32 weights
+  and int32 ids.
+
+Everything is drawn on the CPU from a seeded ``torch.Generator`` so that the
+same seed gives the same bits on every machine (GPU random streams differ
+between devices). Normal draws are made in fp32 and rounded to bf16 before
+the bf16 scaling, which is the same distribution as drawing bf16 directly. The top-K selection uses a stable descending sort, so equal
+probabilities go to the lower expert id. This module is shared by the tests
+and the benchmark; it holds the page's input recipe and nothing of the
+forward computation itself.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Shape:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    K: int
+
+    @property
+    def flop(self) -> int:
+        """Algorithmic FLOP of one forward: 2*T*K*H*(2I) + 2*T*K*I*H."""
+        return 6 * self.T * self.K * self.H * self.I
+
+
+# The five workloads: a tiny case, and four rows of the atrex-bench #009
+# "Shapes" table (T=4195/H=2048/I=2048/E=8/top-2; T=1/H=2048/I=768/E=128/top-8;
+# T=8192/H=4096/I=384/E=128/top-8; T=15381/H=4096/I=4096/E=8/top-2).
+SHAPES = {
+    "tiny": Shape("tiny", 64, 512, 256, 8, 2),
+    "prefill": Shape("prefill", 4195, 2048, 2048, 8, 2),
+    "decode": Shape("decode", 1, 2048, 768, 128, 8),
+    "wide": Shape("wide", 8192, 4096, 384, 128, 8),
+    "large": Shape("large", 15381, 4096, 4096, 8, 2),
+}
+
+
+def topk_routing(logits: torch.Tensor, K: int):
+    """Softmax over experts, K largest (ties to the lower id), renormalised."""
+    probs = logits.float().softmax(dim=-1)
+    vals, idx = torch.sort(probs, dim=-1, descending=True, stable=True)
+    w = vals[:, :K]
+    w = (w / w.sum(dim=-1, keepdim=True)).to(torch.float32)
+    return w.contiguous(), idx[:, :K].to(torch.int32).contiguous()
+
+
+def _randn_bf16(shape, g: torch.Generator) -> torch.Tensor:
+    """N(0,1) rounded to bf16 (drawn in fp32: several times faster on the CPU
+    than drawing bf16 directly, same distribution)."""
+    return torch.randn(shape, dtype=torch.float32, generator=g).to(torch.bfloat16)
+
+
+def make_inputs(T: int, H: int, I: int, E: int, K: int, seed: int = 0) -> dict:
+    """CPU tensors: hidden bf16 [T,H], w1 bf16 [E,2I,H], w2 bf16 [E,H,I],
+    topk_weights fp32 [T,K], topk_ids int32 [T,K], router_logits fp32 [T,E]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    hidden = _randn_bf16((T, H), g) * 0.1
+    w1 = _randn_bf16((E, 2 * I, H), g) * H ** (-0.5)
+    w2 = _randn_bf16((E, H, I), g) * I ** (-0.5)
+    logits = torch.randn(T, E, dtype=torch.float32, generator=g)
+    tw, ids = topk_routing(logits, K)
+    return {"hidden_states": hidden, "w1": w1, "w2": w2, "topk_weights": tw,
+            "topk_ids": ids, "router_logits": logits}
+
+
+def make_shape_inputs(name: str, seed: int = 0) -> dict:
+    s = SHAPES[name]
+    return make_inputs(s.T, s.H, s.I, s.E, s.K, seed=seed)
+
+
+def bf16_bits(t: torch.Tensor):
+    """Raw bf16 bits of a CPU bf16 tensor as a numpy uint16 array."""
+    import numpy as np
+
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)

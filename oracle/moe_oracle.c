@@ -1,0 +1,266 @@
+/*
+ * Plain CPU oracle for the fused Mixture-of-Experts forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously correct
+ * definition that the GPU library is checked against. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it. It shares
+ * no code, header, table or helper with the HIP library, and the HIP library
+ * never calls it.
+ *
+ * Sources (cited by page title and section):
+ *   [atrex-009]  atrex-bench operator #009 "fused_moe", section "Reference
+ *                Implementation" (Model.forward): for each expert, the tokens
+ *                routed to it are taken in fp32, multiplied by w1[e] (rows
+ *                0..I-1 gate, rows I..2I-1 up; F.linear, i.e. x times w1[e]
+ *                transposed), activated as silu(gate)*up, multiplied by w2[e]
+ *                (again F.linear) and added, scaled by the routing weight,
+ *                into an fp32 zero-initialised [T,H] output.
+ *   [tpu-ref]    tpu-inference fused_moe v1 kernel.py, function ref_moe: the
+ *                same computation walked per token, per chosen expert, with
+ *                the per-token outputs summed with the top-k weights.
+ *   [tpu-scatter] tpu-inference fused_moe v1 kernel.py, start_a2a_scatter:
+ *                (token, k) pairs are placed into per-expert contiguous
+ *                buffers by walking tokens in order and, inside a token, the
+ *                k choices in order, bumping a per-expert cursor. This fixes
+ *                the stable order used by the routing oracle below.
+ *
+ * Readings taken where the pages are silent (each restated in the design
+ * notes): the combine adds the K weighted expert outputs in k order from 0;
+ * the dot products accumulate in fp32 in ascending index order; silu(g) is
+ * g / (1 + exp(-g)); the routing weights are used as given (never
+ * renormalised here); in bf16-intermediate mode the activation silu(g)*u is
+ * rounded to bf16 (round to nearest, ties to even) before the down
+ * projection, mirroring the GPU's declared storage precision.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math), so
+ * every fp32 operation is a separately rounded IEEE operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> fp32 (bf16 is the upper half of an IEEE binary32)          */
+/* ------------------------------------------------------------------ */
+
+static float ora_bf16_to_f32(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round to nearest even. NaN stays NaN (quiet bit forced). */
+static uint16_t ora_f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u) {
+    return (uint16_t)((u >> 16) | 0x0040u);
+  }
+  uint32_t lsb = (u >> 16) & 1u;
+  uint32_t rounded = u + 0x7fffu + lsb;
+  return (uint16_t)(rounded >> 16);
+}
+
+void oracle_f32_to_bf16(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_f32_to_bf16_rne(in[i]);
+}
+
+void oracle_bf16_to_f32(const uint16_t* in, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_bf16_to_f32(in[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Routing oracle                                                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Groups the T*K (token, k) slots by expert, in the stable token-major,
+ * k-minor order of [tpu-scatter], each expert's group padded up to a
+ * multiple of the row tile M.
+ *
+ *   counts[e]      number of slots f = t*K + k with ids[f] == e
+ *   offsets[e]     exclusive prefix sum of roundup(counts, M); offsets[E]
+ *                  is the padded total P
+ *   sorted[r]      slot f at padded row r; pad rows hold -1   (length P)
+ *   slot_of[f]     padded row of slot f; -1 if ids[f] is outside [0, E)
+ *   tile_expert[j] expert owning rows [j*M, (j+1)*M), j < P/M
+ *   *num_tiles     P / M
+ *
+ * Returns 0, or -1 if sorted_cap < P or tile_cap < P/M.
+ */
+int oracle_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int64_t M,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted, int64_t sorted_cap,
+                 int32_t* slot_of, int32_t* tile_expert, int64_t tile_cap,
+                 int32_t* num_tiles) {
+  const int64_t n = T * K;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t f = 0; f < n; ++f) {
+    int32_t e = ids[f];
+    if (e >= 0 && e < E) counts[e] += 1;
+  }
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t padded = ((counts[e] + M - 1) / M) * M;
+    offsets[e + 1] = (int32_t)(offsets[e] + padded);
+  }
+  const int64_t P = offsets[E];
+  if (P > sorted_cap || P / M > tile_cap) return -1;
+  for (int64_t r = 0; r < P; ++r) sorted[r] = -1;
+  int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+  for (int64_t f = 0; f < n; ++f) { /* ascending f: token-major, k-minor */
+    int32_t e = ids[f];
+    if (e < 0 || e >= E) {
+      slot_of[f] = -1;
+      continue;
+    }
+    int64_t r = offsets[e] + fill[e];
+    fill[e] += 1;
+    sorted[r] = (int32_t)f;
+    slot_of[f] = (int32_t)r;
+  }
+  free(fill);
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t j = offsets[e] / M; j < offsets[e + 1] / M; ++j) tile_expert[j] = (int32_t)e;
+  *num_tiles = (int32_t)(P / M);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* One expert applied to one token, fp32 ([atrex-009] Model.forward)   */
+/* ------------------------------------------------------------------ */
+
+/*
+ * act[i] = silu(g[i]) * u[i] with g[i] = sum_h x[h]*w1[e,i,h] and
+ * u[i] = sum_h x[h]*w1[e,I+i,h], fp32, h ascending. If bf16_inter, act is
+ * rounded to bf16 (RNE) and returned widened back to fp32.
+ */
+static void ora_expert_act_f32(const uint16_t* x, const uint16_t* w1e, int64_t H, int64_t I,
+                               int bf16_inter, float* act) {
+  for (int64_t i = 0; i < I; ++i) {
+    const uint16_t* wg = w1e + i * H;
+    const uint16_t* wu = w1e + (I + i) * H;
+    float g = 0.0f, u = 0.0f;
+    for (int64_t h = 0; h < H; ++h) {
+      float xv = ora_bf16_to_f32(x[h]);
+      g = g + xv * ora_bf16_to_f32(wg[h]);
+      u = u + xv * ora_bf16_to_f32(wu[h]);
+    }
+    float s = g / (1.0f + expf(-g));
+    float a = s * u;
+    if (bf16_inter) a = ora_bf16_to_f32(ora_f32_to_bf16_rne(a));
+    act[i] = a;
+  }
+}
+
+/* y[h] = sum_i act[i] * w2[e,h,i], fp32, i ascending. */
+static void ora_expert_down_f32(const float* act, const uint16_t* w2e, int64_t H, int64_t I,
+                                float* y) {
+  for (int64_t h = 0; h < H; ++h) {
+    const uint16_t* wr = w2e + h * I;
+    float acc = 0.0f;
+    for (int64_t i = 0; i < I; ++i) acc = acc + act[i] * ora_bf16_to_f32(wr[i]);
+    y[h] = acc;
+  }
+}
+
+/*
+ * Full forward, fp32 ([atrex-009] Model.forward, [tpu-ref] ref_moe):
+ *   out[t,h] = sum over k = 0..K-1 (in that order, from 0) of
+ *              topk_weights[t,k] * y_{t,k}[h]
+ * Slots whose id lies outside [0, E) contribute nothing.
+ * x: bf16 [T,H]; w1: bf16 [E,2I,H]; w2: bf16 [E,H,I]; out: fp32 [T,H].
+ */
+void oracle_moe_forward(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                        const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                        int64_t H, int64_t I, int64_t E, int64_t K, int bf16_inter,
+                        float* out) {
+#pragma omp parallel
+  {
+    float* act = (float*)malloc((size_t)I * sizeof(float));
+    float* y = (float*)malloc((size_t)H * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      float* o = out + t * H;
+      for (int64_t h = 0; h < H; ++h) o[h] = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        int32_t e = topk_ids[t * K + k];
+        if (e < 0 || e >= E) continue;
+        float w = topk_weights[t * K + k];
+        ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, bf16_inter, act);
+        ora_expert_down_f32(act, w2 + (int64_t)e * H * I, H, I, y);
+        for (int64_t h = 0; h < H; ++h) o[h] = o[h] + w * y[h];
+      }
+    }
+    free(act);
+    free(y);
+  }
+}
+
+/*
+ * The activation of every slot f = t*K + k as bf16 bits [T*K, I]
+ * (bf16-intermediate mode), for checking the stored intermediate. Slots
+ * with an out-of-range id are left as zero.
+ */
+void oracle_slot_act_bf16(const uint16_t* x, const uint16_t* w1, const int32_t* topk_ids,
+                          int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                          uint16_t* act_out) {
+#pragma omp parallel
+  {
+    float* act = (float*)malloc((size_t)I * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t f = 0; f < T * K; ++f) {
+      int64_t t = f / K;
+      int32_t e = topk_ids[f];
+      uint16_t* dst = act_out + f * I;
+      if (e < 0 || e >= E) {
+        for (int64_t i = 0; i < I; ++i) dst[i] = 0;
+        continue;
+      }
+      ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, 0, act);
+      for (int64_t i = 0; i < I; ++i) dst[i] = ora_f32_to_bf16_rne(act[i]);
+    }
+    free(act);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* fp64 version of the same definition, for pinning the fp32 oracle    */
+/* ------------------------------------------------------------------ */
+
+void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                            const double* topk_weights, const int32_t* topk_ids, int64_t T,
+                            int64_t H, int64_t I, int64_t E, int64_t K, double* out) {
+#pragma omp parallel
+  {
+    double* act = (double*)malloc((size_t)I * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      double* o = out + t * H;
+      for (int64_t h = 0; h < H; ++h) o[h] = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        int32_t e = topk_ids[t * K + k];
+        if (e < 0 || e >= E) continue;
+        double w = topk_weights[t * K + k];
+        const uint16_t* w1e = w1 + (int64_t)e * 2 * I * H;
+        const uint16_t* w2e = w2 + (int64_t)e * H * I;
+        for (int64_t i = 0; i < I; ++i) {
+          double g = 0.0, u = 0.0;
+          for (int64_t h = 0; h < H; ++h) {
+            double xv = (double)ora_bf16_to_f32(x[t * H + h]);
+            g += xv * (double)ora_bf16_to_f32(w1e[i * H + h]);
+            u += xv * (double)ora_bf16_to_f32(w1e[(I + i) * H + h]);
+          }
+          act[i] = g / (1.0 + exp(-g)) * u;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i) acc += act[i] * (double)ora_bf16_to_f32(w2e[h * I + i]);
+          o[h] += w * acc;
+        }
+      }
+    }
+    free(act);
+  }
+}
