@@ -1,0 +1,221 @@
+"""Benchmark of the fused MoE forward on one MI355X.
+
+One step = one call of the whole forward (routing, grouped gate/up GEMM with
+SiLU, grouped down GEMM, combine; or the weight-streaming path for a single
+decode token) on seeded synthetic inputs already resident in HBM. Inputs
+follow the atrex-bench operator #009 "Input Generation" recipe; the default
+workload is its shapes-table row T=4195, H=2048, I=2048, E=8, top-2.
+
+To keep the weights from being served out of the 256 MB last-level cache
+between steps, every step uses the next of R device copies of the expert
+weights (R chosen so the copies together exceed 512 MB), as consecutive MoE
+layers of a model would.
+
+Prints one JSON line (rank 0, one GPU). Besides the required fields it
+carries ``roofline`` for the dominant kernel (timed on its own with HIP
+events on the stream it runs on) and ``cpu_baseline`` (the CPU oracle on a
+bounded sample of the same inputs, on this host's cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import moe_topk_ids_amd as moe
+from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+METRIC = "fused-MoE bf16 TFLOP/s and µs/call per shape; % of MFMA/HBM roofline at 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# atrex-bench #009 shapes table, T_Prod of the production kernel on its "XPU-A"
+# hardware (another machine: context only), in microseconds.
+PAGE_T_PROD_US = {"prefill": 1600.0, "decode": 116.9, "wide": 5690.0, "large": 18640.0}
+PATHS = {
+    "default": None,
+    "slot": moe.FLAG_FORCE_GROUPED,
+    "atomic": moe.FLAG_FORCE_GROUPED | moe.FLAG_ATOMIC_COMBINE,
+    "decode": moe.FLAG_FORCE_DECODE,
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "moe_topk_ids_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source (else None)."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))[f"{kernel}:{workload}"]
+    except (KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(*rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(d: dict, s, budget_s: float):
+    """The oracle as it stands on a leading sample of tokens sized to ~budget_s."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    x = bf16_bits(d["hidden_states"])
+    w1, w2 = bf16_bits(d["w1"]), bf16_bits(d["w2"])
+    tw, ids = d["topk_weights"].numpy(), d["topk_ids"].numpy()
+    calib = min(s.T, 8)
+    t0 = time.perf_counter()
+    oracle.moe_forward(x[:calib], w1, w2, tw[:calib], ids[:calib])
+    per_tok = (time.perf_counter() - t0) / calib
+    n = int(min(s.T, max(calib, budget_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.moe_forward(x[:n], w1, w2, tw[:n], ids[:n])
+    dt = time.perf_counter() - t0
+    flop = 6.0 * n * s.K * s.H * s.I
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens (same inputs), fp32 C oracle, {dt:.2f} s",
+            "us_per_call_extrapolated": dt / n * s.T * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=list(SHAPES))
+    ap.add_argument("--path", default="default", choices=list(PATHS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-rotate", action="store_true", help="reuse one weight copy every step")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.load_library()
+
+    s = SHAPES[args.workload]
+    flags = PATHS[args.path]
+    log(f"[bench] workload {s} path {args.path}: generating inputs")
+    d = make_inputs(s.T, s.H, s.I, s.E, s.K, seed=0)
+    dev = {k: v.cuda() for k, v in d.items()}
+    touched = len(np.unique(d["topk_ids"].numpy()))
+    wbytes_touched = touched * 3 * s.H * s.I * 2
+    copies = 1 if args.no_rotate else max(1, min(8, -(-512 * 2 ** 20 // wbytes_touched)))
+    w1s = [dev["w1"]] + [dev["w1"].clone() for _ in range(copies - 1)]
+    w2s = [dev["w2"]] + [dev["w2"].clone() for _ in range(copies - 1)]
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        moe.moe_forward(dev["hidden_states"], w1s[i % copies], w2s[i % copies],
+                        dev["topk_weights"], dev["topk_ids"], out=out, flags=flags)
+
+    log(f"[bench] warmup {args.warmup} (weight copies: {copies})")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_wall * 1e3:.1f} us/step wall, {ms_event * 1e3:.1f} us/step events")
+
+    # ---- dominant kernel, timed on its own ----
+    uses_decode = moe.moe_uses_decode_path(s.T, s.H, s.I, s.E, s.K, flags or 0)
+    if uses_decode:
+        kernel = "decode_path"
+        alg_bytes = touched * 3 * s.H * s.I * 2 + s.T * s.H * 2 + s.T * s.H * 4 + s.T * s.K * 8
+        dur_ms = ms_event
+        achieved = alg_bytes / (dur_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "decode_gateup+decode_down (whole decode path)",
+                "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS,
+                "algorithmic_bytes": alg_bytes, "avg_launch_us": dur_ms * 1e3}
+    else:
+        kernel = "grouped_gemm_gate_up_silu"
+        M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
+        r = moe.moe_route(dev["topk_ids"], s.E, M)
+        act = torch.empty((r["capacity"], s.I), dtype=torch.bfloat16, device="cuda")
+        for i in range(3):
+            moe.moe_gemm1_silu(dev["hidden_states"], w1s[i % copies], r, s.K, M, act=act)
+        reps = max(args.steps, 20)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            moe.moe_gemm1_silu(dev["hidden_states"], w1s[i % copies], r, s.K, M, act=act)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        dur_ms = ev0.elapsed_time(ev1) / reps
+        alg_flop = 4.0 * s.T * s.K * s.H * s.I
+        achieved = alg_flop / (dur_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kernel, "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "algorithmic_flop": alg_flop, "avg_launch_us": dur_ms * 1e3}
+        log(f"[bench] {kernel}: {dur_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s")
+    roof["traffic"] = traffic_for(kernel, args.workload)
+
+    flop = float(s.flop)
+    value = flop / (ms_wall * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_wall,
+        "us_per_call": ms_wall * 1e3,
+        "us_per_call_events": ms_event * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (PAGE_T_PROD_US[args.workload] / (ms_wall * 1e3)
+                        if args.workload in PAGE_T_PROD_US else None),
+        "vs_baseline_note": ("page's production time on its own 'XPU-A' hardware for this "
+                             "shapes-table row (context, not a target)"),
+        "dtype": "bf16",
+        "data": "synthetic (seeded, atrex-bench #009 input recipe)",
+        "config": {"workload": f"{s.name}: T={s.T} H={s.H} I={s.I} E={s.E} top_k={s.K}",
+                   "T": s.T, "H": s.H, "I": s.I, "E": s.E, "top_k": s.K,
+                   "path": args.path, "weight_copies": copies,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(d, s, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

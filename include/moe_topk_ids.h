@@ -1,0 +1,166 @@
+/*
+ * moe_topk_ids: fused Mixture-of-Experts forward for AMD Instinct MI355X
+ * (gfx950), as a C ABI over plain device pointers.
+ *
+ * What is computed (atrex-bench operator #009 "fused_moe", section
+ * "Reference Implementation"; the same computation as ref_moe in
+ * tpu-inference's fused_moe v1 kernel.py): for every token t and each of its
+ * K chosen experts e = topk_ids[t,k] with routing weight w = topk_weights[t,k],
+ *
+ *     g = x[t] . W1[e, 0:I, :]^T          (gate, fp32 accumulation)
+ *     u = x[t] . W1[e, I:2I, :]^T         (up)
+ *     a = silu(g) * u                     (stored as bf16, round-to-nearest-even)
+ *     y = a . W2[e]^T                     (fp32 accumulation)
+ *     out[t] = sum over k of w * y        (fp32)
+ *
+ * The routing ids and weights are inputs: the softmax / top-k / renormalise
+ * step that produces them (the "Input Generation" section of the same page)
+ * happens before this library is called. Weights are used as given.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers on the current HIP device,
+ *    owned by the caller; nothing is retained after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without waiting for it, unless a flag says
+ *    otherwise. Buffers must stay alive until the stream has passed the work.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code; moe_last_error()
+ *    then gives a message for the calling thread.
+ *  - Layouts are dense row-major:
+ *      hidden        bf16  [T, H]
+ *      w1            bf16  [E, 2I, H]   rows 0..I-1 gate, rows I..2I-1 up
+ *      w2            bf16  [E, H, I]
+ *      topk_weights  fp32  [T, K]
+ *      topk_ids      int32 [T, K]
+ *      out           fp32  [T, H]       fully overwritten
+ *  - Preconditions: H and I are multiples of 128 (the same alignment rule
+ *    the tpu-inference kernel enforces on hidden and intermediate sizes);
+ *    1 <= K <= E <= 1024; T >= 0. T == 0 is a successful no-op.
+ *  - Ids are expected distinct per token and inside [0, E). An id outside
+ *    [0, E) never causes an out-of-bounds access: that (t,k) pair is dropped
+ *    (contributes nothing). With MOE_FLAG_VALIDATE_IDS the call additionally
+ *    synchronises the stream and returns MOE_ERR_INVALID_ARG if any id was
+ *    out of range or repeated within a token.
+ */
+#ifndef MOE_TOPK_IDS_H
+#define MOE_TOPK_IDS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer with T > 0, bad sizes, K > E, bad ids */
+#define MOE_ERR_UNSUPPORTED (-2) /* H or I not a multiple of 128, E > 1024, ... */
+#define MOE_ERR_HIP (-3)         /* a HIP runtime call failed */
+#define MOE_ERR_ALLOC (-4)       /* device allocation of the internal workspace failed */
+#define MOE_ERR_WORKSPACE (-5)   /* caller workspace too small or misaligned */
+
+/* Combine the K expert outputs with fp32 atomic adds straight from the down
+ * projection into a zeroed `out`, instead of the default deterministic
+ * per-(token,k) slot write followed by a weighted sum in k order. The order
+ * of the adds is not fixed; for K <= 2 the result is still run-to-run
+ * identical and equal to the default path's bits (0 + a + b in either order,
+ * every add rounded to nearest even). */
+#define MOE_FLAG_ATOMIC_COMBINE 1u
+/* Force the grouped (routing + two grouped GEMMs) path. */
+#define MOE_FLAG_FORCE_GROUPED 2u
+/* Force the small-batch weight-streaming path. */
+#define MOE_FLAG_FORCE_DECODE 4u
+/* Synchronise the stream after every stage and name the first stage whose
+ * kernels failed in moe_last_error(). */
+#define MOE_FLAG_DEBUG_SYNC 8u
+/* Check ids on the device; see the preconditions above. Synchronises. */
+#define MOE_FLAG_VALIDATE_IDS 16u
+
+/*
+ * The fused forward: out = sum_k topk_weights[:,k] * Expert_{topk_ids[:,k]}(hidden).
+ * Uses a per-device workspace that the library allocates on first use and
+ * grows as needed (freed by moe_release); the first call for a new maximum
+ * size allocates and is therefore not graph-capture safe. The combine mode
+ * comes from the environment variable MOE_COMBINE ("slot", the default, or
+ * "atomic"), read once.
+ */
+int moe_forward(const void* hidden, const void* w1, const void* w2,
+                const float* topk_weights, const int32_t* topk_ids,
+                int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                float* out, void* stream);
+
+/*
+ * As moe_forward, with explicit flags (MOE_FLAG_*) and an optional caller
+ * workspace. If `workspace` is NULL the internal workspace is used; else it
+ * must be a device buffer of at least moe_workspace_bytes(...) bytes, 256-byte
+ * aligned, used exclusively by this call until the stream passes it. With a
+ * caller workspace the call performs no allocation.
+ */
+int moe_forward_ex(const void* hidden, const void* w1, const void* w2,
+                   const float* topk_weights, const int32_t* topk_ids,
+                   int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                   float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Bytes of workspace moe_forward_ex needs for these sizes and flags
+ * (0 for T == 0). Returns 0 and sets the last error on invalid sizes. */
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                           uint32_t flags);
+
+/* The row tile M that the grouped path pads each expert's rows to, for these
+ * sizes and flags (the value moe_route must be given to reproduce the
+ * forward's routing). Returns a negative MOE_ERR_* code on invalid sizes. */
+int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
+
+/* 1 if moe_forward_ex would take the small-batch weight-streaming path for
+ * these sizes and flags, 0 if the grouped path, negative MOE_ERR_* on
+ * invalid sizes. */
+int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
+
+/*
+ * The routing step alone (the grouping that tpu-inference's start_a2a_scatter
+ * performs when it places each (token, k) pair into its expert's contiguous
+ * buffer, walking tokens in order and k in order inside a token). With slot
+ * f = t*K + k:
+ *   counts[E]        slots per expert (ids outside [0,E) are not counted)
+ *   offsets[E+1]     exclusive prefix sums of counts rounded up to m_tile
+ *   sorted[cap]      padded row -> slot f, grouped by expert, ascending f
+ *                    inside an expert; rows past an expert's count up to
+ *                    its padded end hold -1. Only rows < offsets[E] are written.
+ *   slot_of[T*K]     slot -> padded row; -1 for a dropped (out-of-range) id
+ *   tile_expert[cap/m_tile]  expert of each m_tile-row tile
+ *   num_tiles[1]     offsets[E] / m_tile
+ * `capacity` is the length of `sorted`; it must be at least
+ * T*K + min(E, T*K)*(m_tile-1). m_tile must be a power of two in [16, 256].
+ * `scratch` is a device buffer of at least moe_route_scratch_bytes(T,K,E)
+ * bytes. Deterministic: the output is a pure function of the ids.
+ */
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E, int32_t m_tile,
+              int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
+              int32_t* tile_expert, int32_t* num_tiles, int64_t capacity,
+              void* scratch, void* stream);
+size_t moe_route_scratch_bytes(int64_t T, int64_t K, int64_t E);
+
+/*
+ * The first grouped GEMM with its fused activation, on routing arrays from
+ * moe_route (same m_tile): for every padded row r < offsets[E] holding slot
+ * f = sorted[r] >= 0, act[r, :] = bf16_rne(silu(g) * u) for token f / K and
+ * expert tile_expert[r / m_tile]; pad rows get zeros. act is bf16
+ * [capacity, I] (row-major); rows >= offsets[E] are not written.
+ * `max_tiles` = capacity / m_tile bounds the launch.
+ */
+int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
+                   const int32_t* tile_expert, const int32_t* num_tiles,
+                   int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int32_t m_tile,
+                   int64_t max_tiles, void* act, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Free the internal workspaces of every device (after synchronising them). */
+void moe_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_TOPK_IDS_H */

@@ -1,0 +1,224 @@
+"""Thin Python binding over the C ABI of ``libmoe_topk_ids.so``.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed
+through ctypes, and every step of the computation runs in the library's HIP
+kernels. The entry points carry the C names (see include/moe_topk_ids.h for
+the contract of each). If the library has not been built the calls raise;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_HIP = -3
+MOE_ERR_ALLOC = -4
+MOE_ERR_WORKSPACE = -5
+
+FLAG_ATOMIC_COMBINE = 1
+FLAG_FORCE_GROUPED = 2
+FLAG_FORCE_DECODE = 4
+FLAG_DEBUG_SYNC = 8
+FLAG_VALIDATE_IDS = 16
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_topk_ids.so")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+def load_library():
+    """Load the HIP library (after torch, so one HIP runtime serves both)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (maps torch's HIP runtime before the library's)
+
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library missing: {LIB_PATH}; build it with "
+                           "`python -m moe_topk_ids_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                            ctypes.c_size_t)
+    lib.moe_forward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, p]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_ex.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, u32, p, sz, p]
+    lib.moe_forward_ex.restype = ctypes.c_int
+    lib.moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, u32]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_m_tile.argtypes = [i64, i64, i64, i64, i64, u32]
+    lib.moe_m_tile.restype = i32
+    lib.moe_uses_decode_path.argtypes = [i64, i64, i64, i64, i64, u32]
+    lib.moe_uses_decode_path.restype = ctypes.c_int
+    lib.moe_route.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, i64, p, p]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route_scratch_bytes.argtypes = [i64, i64, i64]
+    lib.moe_route_scratch_bytes.restype = sz
+    lib.moe_gemm1_silu.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, i64, p, p]
+    lib.moe_gemm1_silu.restype = ctypes.c_int
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_release.argtypes = []
+    lib.moe_release.restype = None
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, load_library().moe_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_forward(hidden_states, w1, w2, topk_weights, topk_ids, out=None, flags=None,
+                workspace=None, stream=None):
+    """out[T,H] fp32 = sum_k topk_weights[:,k] * expert_{topk_ids[:,k]}(hidden_states).
+
+    ``flags=None`` calls ``moe_forward`` (internal workspace, MOE_COMBINE from
+    the environment); otherwise ``moe_forward_ex`` with these flags and the
+    optional ``workspace`` (a uint8 device tensor).
+    """
+    import torch
+
+    lib = load_library()
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(w1, "w1", torch.bfloat16, 3)
+    _need(w2, "w2", torch.bfloat16, 3)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, H = hidden_states.shape
+    E, I2, H1 = w1.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    if H1 != H or I2 % 2 or tuple(w2.shape) != (E, H, I) or tuple(topk_weights.shape) != (T, K) \
+            or topk_ids.shape[0] != T:
+        raise ValueError("inconsistent shapes: hidden %s w1 %s w2 %s weights %s ids %s" % (
+            tuple(hidden_states.shape), tuple(w1.shape), tuple(w2.shape),
+            tuple(topk_weights.shape), tuple(topk_ids.shape)))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=hidden_states.device)
+    else:
+        _need(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out must be [T, H]")
+    args = (_ptr(hidden_states), _ptr(w1), _ptr(w2), _ptr(topk_weights), _ptr(topk_ids),
+            T, H, I, E, K, _ptr(out))
+    if flags is None and workspace is None:
+        _check(lib.moe_forward(*args, _stream(stream)))
+    else:
+        ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+        if workspace is not None:
+            _need(workspace, "workspace", torch.uint8, 1)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+        _check(lib.moe_forward_ex(*args, ctypes.c_uint32(flags or 0), ws_ptr,
+                                  ctypes.c_size_t(ws_bytes), _stream(stream)))
+    return out
+
+
+def moe_workspace_bytes(T, H, I, E, K, flags=0) -> int:
+    return int(load_library().moe_workspace_bytes(T, H, I, E, K, flags))
+
+
+def moe_m_tile(T, H, I, E, K, flags=0) -> int:
+    v = int(load_library().moe_m_tile(T, H, I, E, K, flags))
+    if v < 0:
+        _check(v)
+    return v
+
+
+def moe_uses_decode_path(T, H, I, E, K, flags=0) -> bool:
+    v = int(load_library().moe_uses_decode_path(T, H, I, E, K, flags))
+    if v < 0:
+        _check(v)
+    return bool(v)
+
+
+def moe_route(topk_ids, E, m_tile, stream=None) -> dict:
+    """Routing arrays (device int32 tensors); see moe_route in the header."""
+    import torch
+
+    lib = load_library()
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, K = topk_ids.shape
+    n = T * K
+    cap = n + min(E, n) * (m_tile - 1)
+    cap = -(-cap // m_tile) * m_tile
+    dev = topk_ids.device
+    r = {
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "sorted": torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+        "slot_of": torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+        "tile_expert": torch.empty(max(cap // m_tile, 1), dtype=torch.int32, device=dev),
+        "num_tiles": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    scratch = torch.empty(max(int(lib.moe_route_scratch_bytes(T, K, E)), 4), dtype=torch.uint8,
+                          device=dev)
+    _check(lib.moe_route(_ptr(topk_ids), T, K, E, m_tile, _ptr(r["counts"]), _ptr(r["offsets"]),
+                         _ptr(r["sorted"]), _ptr(r["slot_of"]), _ptr(r["tile_expert"]),
+                         _ptr(r["num_tiles"]), cap, _ptr(scratch), _stream(stream)))
+    r["capacity"] = cap
+    r["_scratch"] = scratch  # keep alive until the stream passes the work
+    return r
+
+
+def moe_gemm1_silu(hidden_states, w1, route: dict, K: int, m_tile: int, act=None, stream=None):
+    """bf16 intermediate [capacity, I] of the grouped gate/up GEMM + SiLU
+    (written into ``act`` if given)."""
+    import torch
+
+    lib = load_library()
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(w1, "w1", torch.bfloat16, 3)
+    T, H = hidden_states.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    cap = route["capacity"]
+    if act is None:
+        act = torch.zeros((max(cap, 1), I), dtype=torch.bfloat16, device=hidden_states.device)
+    else:
+        _need(act, "act", torch.bfloat16, 2)
+        if act.shape[0] < cap or act.shape[1] != I:
+            raise ValueError("act must be at least [capacity, I]")
+    _check(lib.moe_gemm1_silu(_ptr(hidden_states), _ptr(w1), _ptr(route["sorted"]),
+                              _ptr(route["tile_expert"]), _ptr(route["num_tiles"]), T, H, I, E, K,
+                              m_tile, cap // m_tile, _ptr(act), _stream(stream)))
+    return act
+
+
+def moe_release():
+    load_library().moe_release()

@@ -1,0 +1,361 @@
+// C ABI of the fused MoE forward: argument validation, workspace layout and
+// ownership, path choice and the launch sequence. Declarations and the
+// contract of every entry point are in include/moe_topk_ids.h.
+//
+// Argument rules follow the ones tpu-inference's fused_moe wrapper raises
+// errors for (top_k within (0, num_experts], hidden and intermediate sizes
+// 128-aligned); errors are reported as codes plus a per-thread message, in
+// the manner of the metrale forward_k2 dispatch refusing unsupported setups
+// with a reason instead of running.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe_topk_ids.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_error(const char* what, hipError_t st) {
+  return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(st));
+}
+
+// Token-slot count above which the grouped path is used.
+constexpr int64_t kDecodeMaxSlots = 16;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0)
+    return set_error(MOE_ERR_INVALID_ARG,
+                     "sizes must be positive (T may be 0): T=%lld H=%lld I=%lld E=%lld K=%lld",
+                     (long long)T, (long long)H, (long long)I, (long long)E, (long long)K);
+  if (K > E)
+    return set_error(MOE_ERR_INVALID_ARG, "top_k=%lld must not exceed num_experts=%lld",
+                     (long long)K, (long long)E);
+  if (E > moe::kMaxExperts)
+    return set_error(MOE_ERR_UNSUPPORTED, "num_experts=%lld exceeds %d", (long long)E,
+                     moe::kMaxExperts);
+  if (H % 128 != 0 || I % 128 != 0)
+    return set_error(MOE_ERR_UNSUPPORTED,
+                     "hidden size %lld and intermediate size %lld must be multiples of 128",
+                     (long long)H, (long long)I);
+  if (T > (int64_t)INT32_MAX / K || T * K > (int64_t)1 << 30)
+    return set_error(MOE_ERR_UNSUPPORTED, "T*K=%lld is too large", (long long)(T * K));
+  return MOE_OK;
+}
+
+bool use_decode(int64_t T, int64_t I, int64_t K, uint32_t flags) {
+  if (!moe::decode_supported(I, K)) return false;
+  if (flags & MOE_FLAG_FORCE_DECODE) return true;
+  if (flags & MOE_FLAG_FORCE_GROUPED) return false;
+  return T * K <= kDecodeMaxSlots;
+}
+
+// Byte offsets of every buffer inside one workspace.
+struct Layout {
+  bool decode = false;
+  moe::GemmCfg g1{}, g2{};
+  int64_t cap = 0, max_tiles = 0, nblk = 0;
+  size_t err = 0, counts = 0, offsets = 0, num_tiles = 0, tile_expert = 0, sorted = 0,
+         slot_of = 0, block_hist = 0, act = 0, y = 0, total = 0;
+};
+
+Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  Layout L;
+  const int64_t n = T * K;
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p = align_up(p + bytes);
+    return at;
+  };
+  L.err = take(sizeof(int32_t));
+  if (use_decode(T, I, K, flags)) {
+    L.decode = true;
+    L.act = take((size_t)n * I * 2);
+    L.total = p;
+    return L;
+  }
+  L.g1 = moe::pick_gemm1_cfg(n, H, I, E);
+  L.g2 = moe::pick_gemm2_cfg(n, H, I, E, L.g1.bm);
+  L.cap = moe::padded_capacity(n, E, L.g1.bm);
+  L.max_tiles = L.cap / L.g1.bm;
+  L.nblk = moe::route_blocks(n);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.num_tiles = take(4);
+  L.tile_expert = take((size_t)L.max_tiles * 4);
+  L.sorted = take((size_t)L.cap * 4);
+  L.slot_of = take((size_t)n * 4);
+  L.block_hist = take((size_t)E * L.nblk * 4);
+  L.act = take((size_t)L.cap * I * 2);
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)n * H * 4);
+  L.total = p;
+  return L;
+}
+
+// ---- internal per-device workspace ----
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+void* g_ws_ptr[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+int internal_workspace(size_t need, void** out) {
+  int dev = 0;
+  hipError_t st = hipGetDevice(&dev);
+  if (st != hipSuccess) return hip_error("hipGetDevice", st);
+  if (dev < 0 || dev >= kMaxDevices) return set_error(MOE_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws_ptr[dev]) {
+      // earlier work may still use the old buffer
+      st = hipDeviceSynchronize();
+      if (st != hipSuccess) return hip_error("hipDeviceSynchronize", st);
+      (void)hipFree(g_ws_ptr[dev]);
+      g_ws_ptr[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+    }
+    void* p = nullptr;
+    st = hipMalloc(&p, need);
+    if (st != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return set_error(MOE_ERR_ALLOC, "hipMalloc(%zu) of the internal workspace failed: %s", need,
+                       hipGetErrorString(st));
+    }
+    g_ws_ptr[dev] = p;
+    g_ws_bytes[dev] = need;
+  }
+  *out = g_ws_ptr[dev];
+  return MOE_OK;
+}
+
+uint32_t env_flags() {
+  static uint32_t flags = [] {
+    const char* c = std::getenv("MOE_COMBINE");
+    return (c && std::strcmp(c, "atomic") == 0) ? MOE_FLAG_ATOMIC_COMBINE : 0u;
+  }();
+  return flags;
+}
+
+int stage_check(uint32_t flags, const char* stage, hipError_t launch, hipStream_t stream) {
+  if (launch != hipSuccess) return hip_error(stage, launch);
+  if (flags & MOE_FLAG_DEBUG_SYNC) {
+    hipError_t st = hipStreamSynchronize(stream);
+    if (st == hipSuccess) st = hipGetLastError();
+    if (st != hipSuccess) return set_error(MOE_ERR_HIP, "stage %s failed: %s", stage, hipGetErrorString(st));
+  }
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  if (check_sizes(T, H, I, E, K) != MOE_OK) return 0;
+  if (T == 0) return 0;
+  return make_layout(T, H, I, E, K, flags).total;
+}
+
+int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  (void)flags;
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  return moe::pick_gemm1_cfg(T * K, H, I, E).bm;
+}
+
+int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  return use_decode(T, I, K, flags) ? 1 : 0;
+}
+
+int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
+                   const int32_t* topk_ids, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                   float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                   void* stream_ptr) {
+  int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!hidden || !w1 || !w2 || !topk_weights || !topk_ids || !out)
+    return set_error(MOE_ERR_INVALID_ARG, "null device pointer with T=%lld", (long long)T);
+  const Layout L = make_layout(T, H, I, E, K, flags);
+  void* ws = workspace;
+  if (ws) {
+    if (workspace_bytes < L.total)
+      return set_error(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                       L.total);
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+      return set_error(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  } else {
+    rc = internal_workspace(L.total, &ws);
+    if (rc != MOE_OK) return rc;
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const auto* x = static_cast<const uint16_t*>(hidden);
+  const auto* wa = static_cast<const uint16_t*>(w1);
+  const auto* wb = static_cast<const uint16_t*>(w2);
+  int32_t* err = at<int32_t>(ws, L.err);
+  const bool validate = (flags & MOE_FLAG_VALIDATE_IDS) != 0;
+  if (validate) {
+    hipError_t st = hipMemsetAsync(err, 0, sizeof(int32_t), stream);
+    if (st == hipSuccess) st = moe::launch_validate_ids(topk_ids, T, K, E, err, stream);
+    if ((rc = stage_check(flags, "validate_ids", st, stream)) != MOE_OK) return rc;
+  }
+
+  if (L.decode) {
+    hipError_t st = moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
+                                       at<uint16_t>(ws, L.act), out, stream);
+    if ((rc = stage_check(flags, "decode", st, stream)) != MOE_OK) return rc;
+  } else {
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* num_tiles = at<int32_t>(ws, L.num_tiles);
+    int32_t* tile_expert = at<int32_t>(ws, L.tile_expert);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* slot_of = at<int32_t>(ws, L.slot_of);
+    int32_t* block_hist = at<int32_t>(ws, L.block_hist);
+    uint16_t* act = at<uint16_t>(ws, L.act);
+    hipError_t st = moe::launch_route(topk_ids, T, K, E, L.g1.bm, block_hist, counts, offsets,
+                                      sorted, slot_of, tile_expert, num_tiles, stream);
+    if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
+    st = moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I, K,
+                                L.max_tiles, act, stream);
+    if ((rc = stage_check(flags, "gemm1_silu", st, stream)) != MOE_OK) return rc;
+    if (flags & MOE_FLAG_ATOMIC_COMBINE) {
+      st = moe::launch_zero(out, T * H, stream);
+      if ((rc = stage_check(flags, "zero_out", st, stream)) != MOE_OK) return rc;
+      st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
+                             K, L.max_tiles, nullptr, out, stream);
+      if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
+    } else {
+      float* y = at<float>(ws, L.y);
+      st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
+                             K, L.max_tiles, y, nullptr, stream);
+      if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
+      st = moe::launch_combine(y, topk_weights, slot_of, T, H, K, out, stream);
+      if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
+    }
+  }
+
+  if (validate) {
+    int32_t host_err = 0;
+    hipError_t st = hipMemcpyAsync(&host_err, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (st == hipSuccess) st = hipStreamSynchronize(stream);
+    if (st != hipSuccess) return hip_error("validate_ids readback", st);
+    if (host_err)
+      return set_error(MOE_ERR_INVALID_ARG,
+                       "topk_ids has an id outside [0, %lld) or a repeated id within a token",
+                       (long long)E);
+  }
+  return MOE_OK;
+}
+
+int moe_forward(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
+                const int32_t* topk_ids, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                float* out, void* stream) {
+  return moe_forward_ex(hidden, w1, w2, topk_weights, topk_ids, T, H, I, E, K, out, env_flags(),
+                        nullptr, 0, stream);
+}
+
+size_t moe_route_scratch_bytes(int64_t T, int64_t K, int64_t E) {
+  if (T < 0 || K <= 0 || E <= 0) return 0;
+  return (size_t)E * moe::route_blocks(T * K) * sizeof(int32_t);
+}
+
+int moe_route(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E, int32_t m_tile,
+              int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
+              int32_t* tile_expert, int32_t* num_tiles, int64_t capacity, void* scratch,
+              void* stream_ptr) {
+  if (T < 0 || K <= 0 || E <= 0 || K > E)
+    return set_error(MOE_ERR_INVALID_ARG, "bad sizes T=%lld K=%lld E=%lld", (long long)T,
+                     (long long)K, (long long)E);
+  if (E > moe::kMaxExperts)
+    return set_error(MOE_ERR_UNSUPPORTED, "num_experts=%lld exceeds %d", (long long)E,
+                     moe::kMaxExperts);
+  if (m_tile < 16 || m_tile > 256 || (m_tile & (m_tile - 1)) != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "m_tile=%d must be a power of two in [16, 256]", m_tile);
+  if (T * K > (int64_t)1 << 30)
+    return set_error(MOE_ERR_UNSUPPORTED, "T*K=%lld is too large", (long long)(T * K));
+  const int64_t n = T * K;
+  const int64_t live = n < E ? n : E;
+  if (capacity < n + live * (m_tile - 1))
+    return set_error(MOE_ERR_INVALID_ARG, "capacity %lld < %lld", (long long)capacity,
+                     (long long)(n + live * (m_tile - 1)));
+  if (!counts || !offsets || !num_tiles || (n > 0 && (!topk_ids || !sorted || !slot_of ||
+                                                      !tile_expert || !scratch)))
+    return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (n == 0) {
+    hipError_t st = hipMemsetAsync(counts, 0, (size_t)E * 4, stream);
+    if (st == hipSuccess) st = hipMemsetAsync(offsets, 0, (size_t)(E + 1) * 4, stream);
+    if (st == hipSuccess) st = hipMemsetAsync(num_tiles, 0, 4, stream);
+    return st == hipSuccess ? MOE_OK : hip_error("moe_route (empty)", st);
+  }
+  hipError_t st = moe::launch_route(topk_ids, T, K, E, m_tile, static_cast<int32_t*>(scratch),
+                                    counts, offsets, sorted, slot_of, tile_expert, num_tiles,
+                                    stream);
+  return st == hipSuccess ? MOE_OK : hip_error("moe_route", st);
+}
+
+int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
+                   const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int64_t H,
+                   int64_t I, int64_t E, int64_t K, int32_t m_tile, int64_t max_tiles, void* act,
+                   void* stream) {
+  int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (m_tile != 64 && m_tile != 128)
+    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64 and 128", m_tile);
+  if (max_tiles < 0 || max_tiles > INT32_MAX)
+    return set_error(MOE_ERR_INVALID_ARG, "max_tiles=%lld", (long long)max_tiles);
+  if (T == 0 || max_tiles == 0) return MOE_OK;
+  if (!hidden || !w1 || !sorted || !tile_expert || !num_tiles || !act)
+    return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
+  hipError_t st = moe::launch_gemm1_silu(
+      moe::GemmCfg{m_tile, 128}, static_cast<const uint16_t*>(hidden),
+      static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
+      static_cast<uint16_t*>(act), static_cast<hipStream_t>(stream));
+  return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
+}
+
+void moe_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (!g_ws_ptr[d]) continue;
+    if (hipSetDevice(d) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws_ptr[d]);
+    }
+    g_ws_ptr[d] = nullptr;
+    g_ws_bytes[d] = 0;
+  }
+  (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of the library.
+// Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Slots handled by one routing workgroup (grows with T*K so that the number
+// of routing workgroups stays at most kRouteMaxBlocks).
+constexpr int kRouteThreads = 256;
+constexpr int kRouteMaxBlocks = 128;
+constexpr int kMaxExperts = 1024;
+
+inline int64_t route_block_slots(int64_t n_slots) {
+  int64_t rb = 1024;
+  while ((n_slots + rb - 1) / rb > kRouteMaxBlocks) rb *= 2;
+  return rb;
+}
+inline int64_t route_blocks(int64_t n_slots) {
+  int64_t rb = route_block_slots(n_slots);
+  return n_slots == 0 ? 0 : (n_slots + rb - 1) / rb;
+}
+
+// Row capacity of the padded, expert-grouped layout: every non-empty expert
+// adds at most m_tile - 1 pad rows, and at most min(E, n_slots) experts are
+// non-empty.
+inline int64_t padded_capacity(int64_t n_slots, int64_t E, int64_t m_tile) {
+  int64_t live = n_slots < E ? n_slots : E;
+  int64_t cap = n_slots + live * (m_tile - 1);
+  return (cap + m_tile - 1) / m_tile * m_tile;
+}
+
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int32_t m_tile,
+                        int32_t* block_hist, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
+                        int32_t* tile_expert, int32_t* num_tiles, hipStream_t stream);
+
+// Tile configuration of the grouped GEMMs, chosen per problem on the host.
+struct GemmCfg {
+  int bm;  // token rows per tile (the routing m_tile)
+  int bn;  // weight rows per tile (GEMM1: half gate, half up)
+};
+
+GemmCfg pick_gemm1_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E);
+GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm);
+
+hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
+                             const int32_t* sorted, const int32_t* tile_expert,
+                             const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
+                             int64_t K, int64_t max_tiles, uint16_t* act, hipStream_t stream);
+
+// Down projection. If `out` is non-null the tile results are scaled by the
+// routing weight and atomically added to out[t, :]; otherwise they are
+// written unscaled to y[f, :] (f = t*K + k).
+hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
+                        const int32_t* sorted, const int32_t* tile_expert,
+                        const int32_t* num_tiles, const float* topk_weights, int64_t H,
+                        int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
+                        hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
+                          int64_t T, int64_t H, int64_t K, float* out, hipStream_t stream);
+hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
+
+// Sets *err_flag to 1 if any id is outside [0, E) or repeats within a token.
+hipError_t launch_validate_ids(const int32_t* ids, int64_t T, int64_t K, int64_t E,
+                               int32_t* err_flag, hipStream_t stream);
+
+bool decode_supported(int64_t I, int64_t K);
+
+hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
+                         const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                         int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,
+                         float* out, hipStream_t stream);
+
+}  // namespace moe

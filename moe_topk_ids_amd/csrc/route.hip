@@ -1,0 +1,202 @@
+// Routing / permutation: groups the T*K (token, k) slots by expert in the
+// stable token-major, k-minor order in which tpu-inference's fused_moe
+// kernel (kernel.py, start_a2a_scatter) fills its per-expert buffers, and
+// pads every expert's group to the GEMM row tile.
+//
+// Two launches, no atomics on the ordering path:
+//   route_count    per workgroup, a per-expert histogram of its slot range
+//                  (LDS atomics: counts do not depend on order);
+//   route_scatter  every workgroup rebuilds the prefix sums it needs from the
+//                  histograms (a few KB from L2), then ranks its slots with
+//                  wave ballots so equal experts keep ascending slot order.
+// Workgroup 0 publishes counts/offsets/num_tiles; pad rows and the
+// tile->expert map are spread over the workgroups by expert.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = kRouteThreads / 64;
+
+__global__ __launch_bounds__(kRouteThreads) void route_count(
+    const int32_t* __restrict__ ids, int64_t n_slots, int32_t E, int64_t rb,
+    int32_t* __restrict__ block_hist) {
+  extern __shared__ int32_t hist[];  // [E]
+  const int tid = threadIdx.x;
+  const int64_t nblk = gridDim.x;
+  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * rb;
+  for (int64_t i = tid; i < rb; i += kRouteThreads) {
+    const int64_t f = base + i;
+    if (f >= n_slots) break;
+    const int32_t e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) block_hist[(int64_t)e * nblk + blockIdx.x] = hist[e];
+}
+
+__device__ inline uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter(
+    const int32_t* __restrict__ ids, int64_t n_slots, int32_t E, int32_t M, int64_t rb,
+    const int32_t* __restrict__ block_hist, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ num_tiles) {
+  // LDS: tot[E], off[E+1], pre[E], run[kWaves][E], part[kRouteThreads]
+  extern __shared__ int32_t lds[];
+  int32_t* tot = lds;
+  int32_t* off = tot + E;
+  int32_t* pre = off + E + 1;
+  int32_t* run = pre + E;
+  __shared__ int32_t part[kRouteThreads];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int64_t nblk = gridDim.x;
+  const int64_t b = blockIdx.x;
+
+  // 1. per expert: total count and the count in earlier workgroups
+  for (int e = tid; e < E; e += kRouteThreads) {
+    const int32_t* h = block_hist + (int64_t)e * nblk;
+    int32_t s = 0, p = 0;
+    for (int64_t j = 0; j < nblk; ++j) {
+      const int32_t v = h[j];
+      p += (j < b) ? v : 0;
+      s += v;
+    }
+    tot[e] = s;
+    pre[e] = p;
+  }
+  for (int i = tid; i < kWaves * E; i += kRouteThreads) run[i] = 0;
+  __syncthreads();
+
+  // 2. exclusive scan over experts of the padded counts
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * per;
+  int32_t local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) local += (tot[e] + M - 1) / M * M;
+  part[tid] = local;
+  __syncthreads();
+  for (int d = 1; d < kRouteThreads; d <<= 1) {
+    const int32_t v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[tid] - local;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    off[e] = acc;
+    acc += (tot[e] + M - 1) / M * M;
+  }
+  if (tid == kRouteThreads - 1) off[E] = part[tid];
+  __syncthreads();
+
+  // 3. metadata: workgroup 0 publishes counts/offsets; pads and the
+  //    tile->expert map are shared out by expert
+  if (b == 0) {
+    for (int e = tid; e < E; e += kRouteThreads) counts[e] = tot[e];
+    for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
+    if (tid == 0) num_tiles[0] = off[E] / M;
+  }
+  for (int64_t e = b; e < E; e += nblk) {
+    const int32_t start = off[e], padded = off[e + 1] - off[e];
+    for (int32_t j = tid; j < padded / M; j += kRouteThreads) tile_expert[start / M + j] = (int32_t)e;
+    for (int32_t r = tot[e] + tid; r < padded; r += kRouteThreads) sorted[start + r] = -1;
+  }
+
+  // 4. per-wave counts over this workgroup's slot range, then each wave's
+  //    first row per expert
+  const int64_t per_wave = rb / kWaves;
+  const int64_t wbase = b * rb + wave * per_wave;
+  int32_t* myrun = run + wave * E;
+  for (int64_t i = lane; i < per_wave; i += 64) {
+    const int64_t f = wbase + i;
+    if (f >= n_slots) break;
+    const int32_t e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&myrun[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int32_t a = off[e] + pre[e];
+    for (int w = 0; w < kWaves; ++w) {
+      const int32_t c = run[w * E + e];
+      run[w * E + e] = a;
+      a += c;
+    }
+  }
+  __syncthreads();
+
+  // 5. stable scatter: chunks of 64 slots in order; rank among equal ids by
+  //    ballot, lowest lane first
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int64_t c0 = 0; c0 < per_wave; c0 += 64) {
+    const int64_t f = wbase + c0 + lane;
+    const bool in = (c0 + lane < per_wave) && (f < n_slots);
+    const int32_t e = in ? ids[f] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t bm = __ballot(set);
+      mask &= set ? bm : ~bm;
+    }
+    if (valid) {
+      const int32_t rank = __popcll(mask & lanemask_lt());
+      const int32_t pos = myrun[e] + rank;
+      sorted[pos] = (int32_t)f;
+      slot_of[f] = pos;
+      if (rank == 0) myrun[e] = pos + __popcll(mask);
+    } else if (in) {
+      slot_of[f] = -1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void validate_ids(const int32_t* __restrict__ ids,
+                                                             int64_t n_slots, int32_t K, int32_t E,
+                                                             int32_t* __restrict__ err_flag) {
+  const int64_t f = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x;
+  if (f >= n_slots) return;
+  const int32_t e = ids[f];
+  int bad = !(e >= 0 && e < E);
+  for (int64_t g = f - f % K; g < f; ++g) bad |= (ids[g] == e);
+  if (bad) atomicOr(err_flag, 1);
+}
+
+}  // namespace
+
+hipError_t launch_validate_ids(const int32_t* ids, int64_t T, int64_t K, int64_t E,
+                               int32_t* err_flag, hipStream_t stream) {
+  const int64_t n = T * K;
+  if (n == 0) return hipSuccess;
+  validate_ids<<<dim3((unsigned)((n + kRouteThreads - 1) / kRouteThreads)), dim3(kRouteThreads), 0,
+                 stream>>>(ids, n, (int32_t)K, (int32_t)E, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int32_t m_tile,
+                        int32_t* block_hist, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
+                        int32_t* tile_expert, int32_t* num_tiles, hipStream_t stream) {
+  const int64_t n = T * K;
+  const int64_t rb = route_block_slots(n);
+  const int64_t nblk = route_blocks(n);
+  if (nblk == 0) return hipSuccess;
+  route_count<<<dim3((unsigned)nblk), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
+      ids, n, (int32_t)E, rb, block_hist);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  const size_t lds = (size_t)(E + E + 1 + E + kWaves * E) * sizeof(int32_t);
+  route_scatter<<<dim3((unsigned)nblk), dim3(kRouteThreads), lds, stream>>>(
+      ids, n, (int32_t)E, m_tile, rb, block_hist, counts, offsets, sorted, slot_of, tile_expert,
+      num_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_topk_ids_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_topk_ids.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted({n for n in names if n.startswith("moe_")})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_topk_ids.so is not built (python -m moe_topk_ids_amd.build)")
+    return moe.load_library()
+
+
+def test_header_declares_the_api():
+    names = _declared_functions()
+    for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
+              "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
+              "moe_uses_decode_path"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"symbol {n} missing"
+
+
+def test_size_validation_without_device(lib):
+    p = ctypes.c_void_p(0)
+    # K > E
+    rc = lib.moe_forward_ex(p, p, p, p, p, 4, 128, 128, 2, 3, p, 0, p, 0, p)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    assert b"top_k" in lib.moe_last_error()
+    # H not a multiple of 128
+    rc = lib.moe_forward_ex(p, p, p, p, p, 4, 100, 128, 8, 2, p, 0, p, 0, p)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+    # negative T
+    rc = lib.moe_forward_ex(p, p, p, p, p, -1, 128, 128, 8, 2, p, 0, p, 0, p)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    # too many experts
+    rc = lib.moe_forward_ex(p, p, p, p, p, 4, 128, 128, 2048, 2, p, 0, p, 0, p)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+    # null pointers with T > 0
+    rc = lib.moe_forward(p, p, p, p, p, 4, 128, 128, 8, 2, p, p)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op success even with null pointers
+    assert lib.moe_forward(p, p, p, p, p, 0, 128, 128, 8, 2, p, p) == moe.MOE_OK
+
+
+def test_route_argument_validation(lib):
+    p = ctypes.c_void_p(0)
+    assert lib.moe_route(p, 4, 2, 8, 48, p, p, p, p, p, p, 1000, p, p) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(p, 4, 2, 8, 64, p, p, p, p, p, p, 10, p, p) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_gemm1_silu(p, p, p, p, p, 4, 128, 128, 8, 2, 32, 1, p, p) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_and_tile_queries(lib):
+    assert moe.moe_workspace_bytes(0, 512, 256, 8, 2) == 0
+    ws_slot = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2)
+    ws_atomic = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, moe.FLAG_ATOMIC_COMBINE)
+    # the slot path holds the fp32 per-slot outputs [T*K, H]
+    assert ws_slot - ws_atomic >= 4195 * 2 * 2048 * 4
+    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128)
+    assert moe.moe_uses_decode_path(1, 2048, 768, 128, 8)
+    assert not moe.moe_uses_decode_path(4195, 2048, 2048, 8, 2)
+    assert moe.moe_uses_decode_path(4195, 2048, 2048, 8, 2, moe.FLAG_FORCE_DECODE)
+    assert not moe.moe_uses_decode_path(1, 2048, 768, 128, 8, moe.FLAG_FORCE_GROUPED)
+    with pytest.raises(moe.MoeError):
+        moe.moe_m_tile(1, 100, 128, 8, 2)

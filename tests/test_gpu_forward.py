@@ -1,0 +1,261 @@
+"""Fused forward on the GPU vs the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import moe_topk_ids_amd as moe
+import oracle
+from gpu_helpers import (assert_close, cpu_inputs, oracle_rows, require_gpu, sample_rows, say,
+                         shape_inputs, to_device)
+from moe_topk_ids_amd.inputs import SHAPES, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {
+    "slot": moe.FLAG_FORCE_GROUPED,
+    "atomic": moe.FLAG_FORCE_GROUPED | moe.FLAG_ATOMIC_COMBINE,
+    "decode": moe.FLAG_FORCE_DECODE,
+}
+
+
+def _run(dd, flags):
+    out = moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                          dd["topk_ids"], flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# Sampled token rows per workload for the oracle (full output for tiny).
+SAMPLES = {"tiny": 64, "prefill": 160, "decode": 1, "wide": 96, "large": 48}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_matches_oracle(name):
+    """Every combine path at the workload's full size; the oracle on sampled
+    token rows (all rows for tiny)."""
+    require_gpu()
+    s = SHAPES[name]
+    d = shape_inputs(name)
+    dd = to_device(d)
+    rows = sample_rows(s.T, SAMPLES[name], seed=1)
+    want = oracle_rows(d, rows)
+    want_b16 = oracle_rows(d, rows, bf16_inter=True)
+    for path in ("default", "slot", "atomic"):
+        say(f"forward {name} path={path}")
+        got = _run(dd, None if path == "default" else PATHS[path])
+        assert_close(got[rows], want, want_b16, f"{name}/{path}")
+    del dd
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_decode_path_matches_oracle(name):
+    """The weight-streaming path on workloads it does not take by default too."""
+    require_gpu()
+    s = SHAPES[name]
+    d = shape_inputs(name)
+    if s.T > 256:  # keep the per-slot path's work small: leading tokens only
+        d = {k: (v[:256] if k in ("hidden_states", "topk_weights", "topk_ids", "router_logits")
+                 else v) for k, v in d.items()}
+    dd = to_device(d)
+    say(f"decode path on {name}")
+    got = _run(dd, moe.FLAG_FORCE_DECODE)
+    rows = sample_rows(got.shape[0], 64, seed=2)
+    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"decode-path/{name}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "wide"])
+def test_intermediate_matches_oracle(name):
+    """GEMM1 + SiLU intermediate vs the oracle's per-slot bf16 activation:
+    at most one bf16 ulp apart, nearly all identical."""
+    require_gpu()
+    s = SHAPES[name]
+    d = shape_inputs(name)
+    dd = to_device(d)
+    M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
+    say(f"intermediate {name} M={M}")
+    r = moe.moe_route(dd["topk_ids"], s.E, M)
+    act = moe.moe_gemm1_silu(dd["hidden_states"], dd["w1"], r, s.K, M)
+    torch.cuda.synchronize()
+    slot_of = r["slot_of"].cpu().numpy()
+    rows = sample_rows(s.T, 48, seed=3)
+    slots = (rows[:, None] * s.K + np.arange(s.K)[None, :]).ravel()
+    got = act.cpu().view(torch.int16).numpy().view(np.uint16)[slot_of[slots]]
+    sub = {k: d[k] for k in d}
+    want = oracle.slot_act_bf16(bf16_bits(sub["hidden_states"])[rows], bf16_bits(sub["w1"]),
+                                sub["topk_ids"].numpy()[rows])
+    gf = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+    wf = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
+    # one bf16 ulp is at most 2**-7 of the value; a little absolute slack
+    # covers values that round from near zero on either side
+    tol = 2.0 ** -7 * np.maximum(np.abs(gf), np.abs(wf)) + 1e-7
+    exact = float(np.mean(got == want))
+    say(f"  identical {exact:.4f}, max |diff| {np.max(np.abs(gf - wf)):.3e}")
+    assert np.all(np.abs(gf - wf) <= tol)
+    assert exact >= 0.97
+    # pad rows of the intermediate are zero
+    offs = r["offsets"].cpu().numpy()
+    counts = r["counts"].cpu().numpy()
+    a16 = act.cpu().view(torch.int16).numpy()
+    for e in range(s.E):
+        pad = a16[offs[e] + counts[e]:offs[e + 1]]
+        assert np.all(pad == 0)
+
+
+def test_slot_path_is_deterministic_and_permutation_invariant():
+    require_gpu()
+    d = shape_inputs("prefill")
+    dd = to_device(d)
+    a = _run(dd, PATHS["slot"])
+    b = _run(dd, PATHS["slot"])
+    assert np.array_equal(a, b)
+    perm = torch.from_numpy(np.random.default_rng(4).permutation(SHAPES["prefill"].T))
+    pd = dict(dd)
+    for k in ("hidden_states", "topk_weights", "topk_ids"):
+        pd[k] = dd[k][perm.cuda()].contiguous()
+    c = _run(pd, PATHS["slot"])
+    assert np.array_equal(c, a[perm.numpy()])
+
+
+@pytest.mark.parametrize("name", ["prefill", "large"])
+def test_atomic_path_is_deterministic_for_top2(name):
+    """With two routing terms per token the atomic combine is 0 + a + b in
+    either order, two-term addition commutes and the hardware atomic add
+    rounds to nearest even: run-to-run identical bits, and the same bits as
+    the slot path's (0 + a) + b."""
+    require_gpu()
+    dd = to_device(shape_inputs(name))
+    a = _run(dd, PATHS["atomic"])
+    b = _run(dd, PATHS["atomic"])
+    assert np.array_equal(a, b)
+    c = _run(dd, PATHS["slot"])
+    assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("T,H,I,E,K", [
+    (1, 128, 128, 1, 1), (37, 128, 256, 4, 4), (129, 256, 128, 16, 1), (1000, 384, 640, 6, 3),
+    (3, 512, 256, 8, 2), (20, 128, 128, 128, 8), (300, 256, 384, 64, 6),
+])
+@pytest.mark.parametrize("path", ["slot", "atomic", "decode"])
+def test_ragged_and_degenerate_shapes(T, H, I, E, K, path):
+    require_gpu()
+    d = cpu_inputs(T, H, I, E, K, seed=T + E)
+    dd = to_device(d)
+    say(f"shape T={T} H={H} I={I} E={E} K={K} path={path}")
+    got = _run(dd, PATHS[path])
+    rows = np.arange(T)
+    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"{T},{H},{I},{E},{K}/{path}")
+
+
+def test_all_tokens_one_expert_and_empty_experts():
+    require_gpu()
+    d = dict(cpu_inputs(700, 256, 256, 16, 2, seed=5))
+    ids = d["topk_ids"].clone()
+    ids[:, 0] = 3
+    ids[:, 1] = torch.where(ids[:, 1] == 3, torch.full_like(ids[:, 1], 9), ids[:, 1]) % 4 + 8
+    d["topk_ids"] = ids.contiguous()
+    dd = to_device(d)
+    rows = np.arange(700)
+    want = oracle_rows(d, rows)
+    for path in ("slot", "atomic"):
+        assert_close(_run(dd, PATHS[path]), want, oracle_rows(d, rows, bf16_inter=True),
+                     f"one-expert/{path}")
+
+
+def test_out_of_range_ids_are_dropped():
+    require_gpu()
+    d = dict(cpu_inputs(64, 512, 256, 8, 2, seed=6))
+    ids = d["topk_ids"].clone()
+    ids[5, 1] = -1
+    ids[9, 0] = 8
+    zeroed = d["topk_weights"].clone()
+    zeroed[5, 1] = 0
+    zeroed[9, 0] = 0
+    bad = dict(d, topk_ids=ids)
+    ref = dict(d, topk_weights=zeroed)
+    rows = np.arange(64)
+    want = oracle_rows(ref, rows)
+    for path in ("slot", "atomic", "decode"):
+        got = _run(to_device(bad), PATHS[path])
+        assert_close(got, want, None, f"dropped-ids/{path}")
+
+
+def test_validate_flag_reports_bad_ids():
+    require_gpu()
+    d = dict(cpu_inputs(64, 512, 256, 8, 2, seed=6))
+    good = to_device(d)
+    moe.moe_forward(**{k: good[k] for k in ("hidden_states", "w1", "w2", "topk_weights",
+                                             "topk_ids")}, flags=moe.FLAG_VALIDATE_IDS)
+    for mutate in ("range", "duplicate"):
+        ids = d["topk_ids"].clone()
+        if mutate == "range":
+            ids[10, 1] = 99
+        else:
+            ids[10, 1] = ids[10, 0]
+        bad = dict(good, topk_ids=ids.cuda())
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_forward(**{k: bad[k] for k in ("hidden_states", "w1", "w2", "topk_weights",
+                                                    "topk_ids")}, flags=moe.FLAG_VALIDATE_IDS)
+        assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_and_errors():
+    require_gpu()
+    d = to_device(cpu_inputs(4, 128, 128, 4, 2))
+    empty = {k: v[:0] for k, v in d.items()}
+    out = moe.moe_forward(empty["hidden_states"], d["w1"], d["w2"], empty["topk_weights"],
+                          empty["topk_ids"])
+    assert out.shape == (0, 128)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward(d["hidden_states"], d["w1"], d["w2"], d["topk_weights"], d["topk_ids"],
+                        flags=0, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert ei.value.code == moe.MOE_ERR_WORKSPACE
+
+
+def test_caller_workspace_and_side_stream():
+    require_gpu()
+    s = SHAPES["tiny"]
+    d = shape_inputs("tiny")
+    dd = to_device(d)
+    ref = _run(dd, PATHS["slot"])
+    nbytes = moe.moe_workspace_bytes(s.T, s.H, s.I, s.E, s.K, PATHS["slot"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                              dd["topk_ids"], flags=PATHS["slot"], workspace=ws)
+    side.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_debug_sync_flag():
+    require_gpu()
+    dd = to_device(shape_inputs("tiny"))
+    a = _run(dd, PATHS["slot"] | moe.FLAG_DEBUG_SYNC)
+    b = _run(dd, PATHS["slot"])
+    assert np.array_equal(a, b)
+
+
+def test_largest_shapes_row():
+    """The largest row of the shapes table (T=45936, H=2048, I=768, E=128,
+    top-8): full-size run, sampled rows against the oracle."""
+    require_gpu()
+    T, H, I, E, K = 45936, 2048, 768, 128, 8
+    d = cpu_inputs(T, H, I, E, K, seed=0)
+    dd = to_device(d)
+    say("forward largest shapes-table row")
+    got = _run(dd, None)
+    rows = sample_rows(T, 32, seed=5)
+    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 "shapes-row-14")
+
+
+def test_single_hip_runtime_is_mapped():
+    """torch and the library share one HIP runtime (stream handles are valid)."""
+    require_gpu()
+    moe.load_library()
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+    assert any("libmoe_topk_ids.so" in line for line in maps.splitlines())

@@ -1,0 +1,88 @@
+"""Routing kernel vs the routing oracle: bit-exact on every array."""
+import numpy as np
+import pytest
+import torch
+
+import moe_topk_ids_amd as moe
+import oracle
+from gpu_helpers import require_gpu, say, shape_inputs
+from moe_topk_ids_amd.inputs import SHAPES
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_route(ids_np: np.ndarray, E: int, M: int, label: str):
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).cuda()
+    say(f"route {label}: T={ids_np.shape[0]} K={ids_np.shape[1]} E={E} M={M}")
+    r = moe.moe_route(ids, E, M)
+    torch.cuda.synchronize()
+    want = oracle.route(ids_np, E, M)
+    P = int(want["offsets"][-1])
+    n = ids_np.size
+    np.testing.assert_array_equal(r["counts"].cpu().numpy(), want["counts"], err_msg="counts")
+    np.testing.assert_array_equal(r["offsets"].cpu().numpy(), want["offsets"], err_msg="offsets")
+    assert int(r["num_tiles"].item()) == want["num_tiles"]
+    np.testing.assert_array_equal(r["sorted"].cpu().numpy()[:P], want["sorted"], err_msg="sorted")
+    np.testing.assert_array_equal(r["slot_of"].cpu().numpy()[:n], want["slot_of"], err_msg="slot_of")
+    np.testing.assert_array_equal(r["tile_expert"].cpu().numpy()[:P // M], want["tile_expert"],
+                                  err_msg="tile_expert")
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_route_bitexact_on_workloads(name):
+    require_gpu()
+    s = SHAPES[name]
+    ids = shape_inputs(name)["topk_ids"].numpy()
+    M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
+    _check_route(ids, s.E, M, name)
+    for other in (64, 128):
+        if other != M:
+            _check_route(ids, s.E, other, f"{name} M={other}")
+
+
+def _rand_ids(T, K, E, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", ["one_expert", "empty_experts", "single_token_e128",
+                                  "ragged_multiblock", "k_equals_e", "out_of_range",
+                                  "many_blocks", "m16", "m256"])
+def test_route_edge_cases(case):
+    require_gpu()
+    rng = np.random.default_rng(7)
+    if case == "one_expert":  # every token's first choice is expert 5
+        ids = _rand_ids(3000, 2, 8, 1)
+        ids[:, 0] = 5
+        ids[:, 1] = np.where(ids[:, 1] == 5, 6, ids[:, 1])
+        _check_route(ids, 8, 128, case)
+    elif case == "empty_experts":
+        ids = (_rand_ids(777, 3, 4, 2) * 5).astype(np.int32)  # only experts 0,5,10,15 of 32
+        _check_route(ids, 32, 64, case)
+    elif case == "single_token_e128":
+        _check_route(_rand_ids(1, 8, 128, 3), 128, 128, case)
+    elif case == "ragged_multiblock":
+        _check_route(_rand_ids(1237, 7, 40, 4), 40, 64, case)
+    elif case == "k_equals_e":
+        _check_route(_rand_ids(501, 8, 8, 5), 8, 128, case)
+    elif case == "out_of_range":
+        ids = _rand_ids(300, 4, 16, 6)
+        ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = -3
+        ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = 16
+        _check_route(ids, 16, 64, case)
+    elif case == "many_blocks":  # the largest workload row on the shapes table
+        _check_route(_rand_ids(45936, 8, 128, 8), 128, 128, case)
+    elif case == "m16":
+        _check_route(_rand_ids(333, 2, 8, 9), 8, 16, case)
+    elif case == "m256":
+        _check_route(_rand_ids(4000, 2, 8, 10), 8, 256, case)
+
+
+def test_route_is_deterministic():
+    require_gpu()
+    ids = torch.from_numpy(_rand_ids(20000, 8, 128, 11)).cuda()
+    a = moe.moe_route(ids, 128, 128)
+    b = moe.moe_route(ids, 128, 128)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "sorted", "slot_of", "tile_expert", "num_tiles"):
+        assert torch.equal(a[k], b[k]), k
