@@ -16,12 +16,18 @@
 // 16 accumulators of a lane hold 4 runs of 4 consecutive output columns for
 // one token row: epilogues store 8-byte bf16 or 16-byte fp32 vectors.
 //
-// Staging: K is consumed 64 bf16 at a time. Global -> registers (16-byte
-// loads, 8 lanes per 128-byte row segment) for step k+1 is in flight while
-// the matrix cores work on step k out of LDS; LDS is double-buffered so one
-// barrier per step suffices. Rows are stored in LDS as 8 chunks of 16 bytes
-// permuted by an XOR of the row index, so that the fragment reads of any 16
-// consecutive rows at the same logical chunk fall on distinct banks.
+// Staging: K is consumed 64 bf16 (128 bytes per row) per step through an
+// NS-deep ring of LDS stages. Each stage is filled by buffer_load_dwordx4
+// with the LDS bit (global -> LDS directly, no register staging): a wave's
+// load writes 1 KB of LDS, 16 bytes per lane, so the 8-chunk XOR permutation
+// of each 128-byte row (chosen so that the fragment reads of any 16
+// consecutive rows at one logical chunk hit distinct banks) is applied on
+// the global side by choosing which chunk each lane fetches. While the
+// matrix cores work on stage k, the loads of stages k+1 .. k+NS-1 are in
+// flight; the vector-memory counter is waited on explicitly, one barrier per
+// step. Rows outside the operand (pad rows of the routing layout, weight
+// rows past N) are read through an out-of-range buffer offset and arrive as
+// zeros.
 //
 // Gate/up pairing (the epilogue needs silu(gate_i) * up_i in one lane): the
 // BN weight rows of a GEMM1 tile are BN/2 gate rows [n0, n0+BN/2) and the
@@ -36,6 +42,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;  // contraction elements per pipeline step (128 bytes per row)
 
@@ -53,8 +60,11 @@ struct GemmArgs {
   int64_t n_out;            // output columns (I for GEMM1, H for GEMM2)
   int64_t w_expert_stride;  // elements per expert in w
   int64_t inter;            // I (GEMM1: offset of the up rows)
+  uint32_t a_bytes;         // bytes of the token operand (GEMM1 gather bound)
   int32_t topk;             // K
   int32_t max_tiles;        // row tiles the grid was sized for
+  int32_t n_tiles;          // weight-row tiles
+  int32_t group_m;          // row tiles per scheduling group
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -71,21 +81,57 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
+// Buffer resource for raw (unstructured) loads: bytes past num_records read
+// as zero, which is how pad rows and out-of-range weight rows are zero-filled
+// without branches.
+__device__ __forceinline__ int32x4_t make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4_t r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)(uint32_t)(a >> 32) & 0xffff;  // stride 0
+  r[2] = (int32_t)num_records;
+  r[3] = 0x00020000;
+  return r;
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= num_records reads zeros
+
+// One 16-byte load per lane straight into LDS: lane i's bytes land at
+// lds_addr + 16*i. lds_addr must be wave-uniform.
+__device__ __forceinline__ void load_lds_b128(int32x4_t rsrc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
-  constexpr int NT = 64 * WGM * WGN;
+  constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;  // token rows per wave
   constexpr int WTN = BN / WGN;  // weight rows per wave
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int CA = BM * 8 / NT;  // 16-byte token chunks per thread per step
-  constexpr int CB = BN * 8 / NT;  // 16-byte weight chunks per thread per step
-  constexpr int RSTEP = NT / 8;    // rows between a thread's consecutive chunks
-  static_assert(CA >= 1 && CB >= 1 && TM >= 1 && TN >= 1, "tile too small");
+  constexpr int LA = BM / (8 * NW);  // 1 KB token-row loads per wave per stage
+  constexpr int LB = BN / (8 * NW);  // 1 KB weight-row loads per wave per stage
+  constexpr int ROWB = BK * 2;       // bytes per staged row
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 1, "tile too small");
   static_assert(MODE != kGateUpSilu || (TN % 2 == 0), "gate/up pairing needs even TN");
+  static_assert(NS >= 2, "at least two stages");
 
-  __shared__ uint4 sA[2][BM * 8];
-  __shared__ uint4 sW[2][BN * 8];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,74 +139,63 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int wm = wave % WGM;
   const int wn = wave / WGM;
 
-  const int mt = blockIdx.x % args.max_tiles;
-  const int ntile = blockIdx.x / args.max_tiles;
+  // XCD-aware tile order: consecutive workgroup ids are dealt round-robin to
+  // the 8 XCDs, so hand each XCD a contiguous run of logical tiles; inside
+  // it, groups of GM row tiles sweep the weight tiles so that the tiles
+  // resident on one XCD share token rows and weight rows in its L2.
+  const int n_tiles = args.n_tiles;
+  const int total = args.max_tiles * n_tiles;
+  const int per_xcd = gridDim.x / 8;
+  const int pid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (pid >= total) return;
+  const int group = pid / (args.group_m * n_tiles);
+  const int first_m = group * args.group_m;
+  const int gsize = min(args.max_tiles - first_m, args.group_m);
+  const int within = pid - group * args.group_m * n_tiles;
+  const int mt = first_m + within % gsize;
+  const int ntile = within / gsize;
   if (mt >= args.num_tiles[0]) return;
   const int e = args.tile_expert[mt];
   const int64_t m0 = (int64_t)mt * BM;
   const int64_t kdim = args.kdim;
 
-  // ---- per-thread global row pointers (fixed over the K loop) ----
-  const int chunk = tid & 7;
-  const uint16_t* arow[CA];
+  // ---- per-lane load offsets (fixed over the K loop) ----
+  // load j of this wave covers staged rows 8*g .. 8*g+7 (g = wave*L + j);
+  // lane -> row 8*g + lane/8, physical chunk lane%8, logical chunk
+  // (lane%8) ^ swz(row): the XOR layout is applied on the global side.
+  int32x4_t rsrc_a, rsrc_b;
+  uint32_t aoff[LA], boff[LB];
+  if (MODE == kGateUpSilu) {
+    rsrc_a = make_rsrc(args.a, args.a_bytes);
+  } else {
+    rsrc_a = make_rsrc(args.a + m0 * kdim, (uint32_t)(BM * kdim * 2));
+  }
+  rsrc_b = make_rsrc(args.w + (int64_t)e * args.w_expert_stride, (uint32_t)(args.w_expert_stride * 2));
 #pragma unroll
-  for (int j = 0; j < CA; ++j) {
-    const int64_t r = m0 + (tid >> 3) + j * RSTEP;
+  for (int j = 0; j < LA; ++j) {
+    const int r = 8 * (wave * LA + j) + (lane >> 3);
+    const uint32_t cb = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     if (MODE == kGateUpSilu) {
-      const int32_t f = args.sorted[r];
-      arow[j] = f >= 0 ? args.a + (int64_t)(f / args.topk) * kdim + chunk * 8 : nullptr;
+      const int32_t f = args.sorted[m0 + r];
+      aoff[j] = f >= 0 ? (uint32_t)((int64_t)(f / args.topk) * kdim * 2) + cb : kOutOfRange;
     } else {
-      arow[j] = args.a + r * kdim + chunk * 8;
+      aoff[j] = (uint32_t)(r * kdim * 2) + cb;
     }
   }
-  const uint16_t* wrow[CB];
-  const uint16_t* wbase = args.w + (int64_t)e * args.w_expert_stride;
 #pragma unroll
-  for (int j = 0; j < CB; ++j) {
-    const int nl = (tid >> 3) + j * RSTEP;
-    int64_t row;
-    bool ok;
+  for (int j = 0; j < LB; ++j) {
+    const int n = 8 * (wave * LB + j) + (lane >> 3);
+    const uint32_t cb = (uint32_t)(((lane & 7) ^ swz(n)) * 16);
     if (MODE == kGateUpSilu) {
       const int64_t n0g = (int64_t)ntile * (BN / 2);
-      row = nl < BN / 2 ? n0g + nl : args.inter + n0g + (nl - BN / 2);
-      ok = true;  // I is a multiple of BN/2
+      const int64_t row = n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
+      boff[j] = (uint32_t)(row * kdim * 2) + cb;
     } else {
-      row = (int64_t)ntile * BN + nl;
-      ok = row < args.n_out;
+      const int64_t row = (int64_t)ntile * BN + n;
+      boff[j] = row < args.n_out ? (uint32_t)(row * kdim * 2) + cb : kOutOfRange;
     }
-    wrow[j] = ok ? wbase + row * kdim + chunk * 8 : nullptr;
   }
-
-  uint4 ra[CA], rw[CB];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int j = 0; j < CA; ++j)
-      ra[j] = arow[j] ? *reinterpret_cast<const uint4*>(arow[j] + k0) : zero4;
-#pragma unroll
-    for (int j = 0; j < CB; ++j)
-      rw[j] = wrow[j] ? *reinterpret_cast<const uint4*>(wrow[j] + k0) : zero4;
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < CA; ++j) {
-      const int r = (tid >> 3) + j * RSTEP;
-      sA[st][r * 8 + (chunk ^ swz(r))] = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const int r = (tid >> 3) + j * RSTEP;
-      sW[st][r * 8 + (chunk ^ swz(r))] = rw[j];
-    }
-  };
-
-  f32x16_t acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
   // LDS row of each of this wave's weight sub-tiles
   int nrow[TN];
@@ -174,13 +209,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     }
   }
 
+  f32x16_t acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
   const int nk = (int)(kdim / BK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
+
+#define MOE_ISSUE_STAGE(buf, kt)                                                              \
+  do {                                                                                        \
+    const uint32_t kb = (uint32_t)(kt) * ROWB;                                                \
+    const uint32_t sb = smem_base + (uint32_t)(buf) * STAGE;                                  \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                           \
+        load_lds_b128(rsrc_a, aoff[j] + kb,                                                   \
+                      __builtin_amdgcn_readfirstlane(sb + (wave * LA + j) * 1024));           \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                           \
+        load_lds_b128(rsrc_b, boff[j] + kb,                                                   \
+                      __builtin_amdgcn_readfirstlane(sb + A_BYTES + (wave * LB + j) * 1024)); \
+  } while (0)
+
+  // prologue: NS-1 stages in flight
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) MOE_ISSUE_STAGE(s, s);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
+    // stage kt has landed once at most the later stages' loads are pending
+    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * (LA + LB)>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is free
+    if (kt + NS - 1 < nk) MOE_ISSUE_STAGE((kt + NS - 1) % NS, kt + NS - 1);
+    const char* sa = smem + (kt % NS) * STAGE;
+    const char* sw = sa + A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
@@ -188,12 +251,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const int r = wm * WTM + tm * 32 + (lane & 31);
-        bt[tm] = __builtin_bit_cast(bf16x8_t, sA[cur][r * 8 + (c ^ swz(r))]);
+        bt[tm] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((c ^ swz(r)) << 4));
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int r = nrow[tn] + (lane & 31);
-        aw[tn] = __builtin_bit_cast(bf16x8_t, sW[cur][r * 8 + (c ^ swz(r))]);
+        aw[tn] = *reinterpret_cast<const bf16x8_t*>(sw + r * ROWB + ((c ^ swz(r)) << 4));
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
@@ -201,9 +264,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
         for (int tm = 0; tm < TM; ++tm)
           acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[tn], bt[tm], acc[tn][tm], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
   }
+#undef MOE_ISSUE_STAGE
 
   // ---- epilogues ----
   // lane holds, for token row (lane & 31) of sub-tile tm, the weight columns
@@ -264,19 +326,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE>
-hipError_t launch_cfg(const GemmArgs& a, int n_tiles, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.max_tiles * n_tiles;
-  if (blocks == 0) return hipSuccess;
-  grouped_gemm<BM, BN, WGM, WGN, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
+template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
+hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
+  const int64_t total = (int64_t)a.max_tiles * a.n_tiles;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+  grouped_gemm<BM, BN, WGM, WGN, NS, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch(GemmCfg cfg, const GemmArgs& a, int n_tiles, hipStream_t stream) {
-  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 2, 2, MODE>(a, n_tiles, stream);
-  if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 2, 2, MODE>(a, n_tiles, stream);
-  if (cfg.bm == 128 && cfg.bn == 256) return launch_cfg<128, 256, 2, 2, MODE>(a, n_tiles, stream);
+hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
+  a.group_m = 8;
+  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 2, 2, 2, MODE>(a, stream);
+  if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 2, 2, 2, MODE>(a, stream);
+  if (cfg.bm == 128 && cfg.bn == 256) return launch_cfg<128, 256, 2, 2, 2, MODE>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -303,7 +367,6 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
                              int64_t K, int64_t max_tiles, uint16_t* act, hipStream_t stream) {
-  (void)T;
   GemmArgs a{};
   a.a = hidden;
   a.w = w1;
@@ -317,8 +380,9 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
   a.inter = I;
   a.topk = (int32_t)K;
   a.max_tiles = (int32_t)max_tiles;
-  const int n_tiles = (int)(I / (cfg.bn / 2));
-  return dispatch<kGateUpSilu>(cfg, a, n_tiles, stream);
+  a.a_bytes = (uint32_t)(T * H * 2);
+  a.n_tiles = (int)(I / (cfg.bn / 2));
+  return dispatch<kGateUpSilu>(cfg, a, stream);
 }
 
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
@@ -340,9 +404,9 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   a.inter = I;
   a.topk = (int32_t)K;
   a.max_tiles = (int32_t)max_tiles;
-  const int n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
-  if (out) return dispatch<kDownAtomic>(cfg, a, n_tiles, stream);
-  return dispatch<kDownSlot>(cfg, a, n_tiles, stream);
+  a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
+  if (out) return dispatch<kDownAtomic>(cfg, a, stream);
+  return dispatch<kDownSlot>(cfg, a, stream);
 }
 
 }  // namespace moe

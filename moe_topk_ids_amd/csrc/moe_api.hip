@@ -58,6 +58,13 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
                      (long long)H, (long long)I);
   if (T > (int64_t)INT32_MAX / K || T * K > (int64_t)1 << 30)
     return set_error(MOE_ERR_UNSUPPORTED, "T*K=%lld is too large", (long long)(T * K));
+  // the GEMMs address the hidden states and one expert's weights through
+  // 32-bit buffer offsets with bit 31 reserved for "out of range"
+  if (T * H * 2 >= ((int64_t)1 << 31) || 3 * I * H * 2 >= ((int64_t)1 << 31))
+    return set_error(MOE_ERR_UNSUPPORTED,
+                     "hidden states (%lld bytes) and one expert's weights (%lld bytes) must each "
+                     "be under 2 GiB",
+                     (long long)(T * H * 2), (long long)(3 * I * H * 2));
   return MOE_OK;
 }
 
