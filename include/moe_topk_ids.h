@@ -146,7 +146,8 @@ size_t moe_route_scratch_bytes(int64_t T, int64_t K, int64_t E);
  * f = sorted[r] >= 0, act[r, :] = bf16_rne(silu(g) * u) for token f / K and
  * expert tile_expert[r / m_tile]; pad rows get zeros. act is bf16
  * [capacity, I] (row-major); rows >= offsets[E] are not written.
- * `max_tiles` = capacity / m_tile bounds the launch.
+ * `max_tiles` = capacity / m_tile bounds the launch. m_tile must be 64, 128
+ * or 256 (the row tiles the grouped GEMMs are built for).
  */
 int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    const int32_t* tile_expert, const int32_t* num_tiles,

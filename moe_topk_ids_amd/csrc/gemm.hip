@@ -44,7 +44,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;  // contraction elements per pipeline step (128 bytes per row)
 
 enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2 };
 
@@ -67,7 +66,15 @@ struct GemmArgs {
   int32_t group_m;          // row tiles per scheduling group
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// XOR permutation of the 16-byte chunks of a staged row (CPR chunks per
+// row). With it the fragment reads of 8 consecutive rows cover a 128-byte
+// bank window and those of 16 consecutive rows a 256-byte window without
+// repeating a bank group, for both row widths used.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // silu(g) * u = g * u / (1 + exp(-g)); exp via the hardware 2^x.
@@ -115,16 +122,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;  // token rows per wave
   constexpr int WTN = BN / WGN;  // weight rows per wave
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int LA = BM / (8 * NW);  // 1 KB token-row loads per wave per stage
-  constexpr int LB = BN / (8 * NW);  // 1 KB weight-row loads per wave per stage
   constexpr int ROWB = BK * 2;       // bytes per staged row
+  constexpr int CPR = ROWB / 16;     // 16-byte chunks per staged row
+  constexpr int RPL = 1024 / ROWB;   // staged rows per 1 KB wave load
+  constexpr int LA = BM / (RPL * NW);  // 1 KB token-row loads per wave per stage
+  constexpr int LB = BN / (RPL * NW);  // 1 KB weight-row loads per wave per stage
+  static_assert(BK == 32 || BK == 64, "BK");
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE = (BM + BN) * ROWB;
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 1, "tile too small");
@@ -160,9 +170,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int64_t kdim = args.kdim;
 
   // ---- per-lane load offsets (fixed over the K loop) ----
-  // load j of this wave covers staged rows 8*g .. 8*g+7 (g = wave*L + j);
-  // lane -> row 8*g + lane/8, physical chunk lane%8, logical chunk
-  // (lane%8) ^ swz(row): the XOR layout is applied on the global side.
+  // load j of this wave covers staged rows RPL*g .. RPL*g+RPL-1 (g = wave*L
+  // + j); lane -> row RPL*g + lane/CPR, physical chunk lane%CPR, logical
+  // chunk (lane%CPR) ^ swz(row): the XOR layout is applied on the global side.
   int32x4_t rsrc_a, rsrc_b;
   uint32_t aoff[LA], boff[LB];
   if (MODE == kGateUpSilu) {
@@ -173,8 +183,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   rsrc_b = make_rsrc(args.w + (int64_t)e * args.w_expert_stride, (uint32_t)(args.w_expert_stride * 2));
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int r = 8 * (wave * LA + j) + (lane >> 3);
-    const uint32_t cb = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    const int r = RPL * (wave * LA + j) + lane / CPR;
+    const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(r)) * 16);
     if (MODE == kGateUpSilu) {
       const int32_t f = args.sorted[m0 + r];
       aoff[j] = f >= 0 ? (uint32_t)((int64_t)(f / args.topk) * kdim * 2) + cb : kOutOfRange;
@@ -184,8 +194,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int n = 8 * (wave * LB + j) + (lane >> 3);
-    const uint32_t cb = (uint32_t)(((lane & 7) ^ swz(n)) * 16);
+    const int n = RPL * (wave * LB + j) + lane / CPR;
+    const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(n)) * 16);
     if (MODE == kGateUpSilu) {
       const int64_t n0g = (int64_t)ntile * (BN / 2);
       const int64_t row = n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
@@ -231,40 +241,73 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
                       __builtin_amdgcn_readfirstlane(sb + A_BYTES + (wave * LB + j) * 1024)); \
   } while (0)
 
-  // prologue: NS-1 stages in flight
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) MOE_ISSUE_STAGE(s, s);
+  // Fragment reads of sub-step kk of the stage in LDS buffer `buf`; the lane
+  // holds 8 consecutive k of its row: chunk 2*kk + lane/32 of the 128-byte row.
+#define MOE_LOAD_FRAGS(F, buf, kk)                                                             \
+  do {                                                                                         \
+    const char* sa_ = smem + (buf) * STAGE;                                                    \
+    const char* sw_ = sa_ + A_BYTES;                                                           \
+    const int c_ = (kk) * 2 + (lane >> 5);                                                     \
+    _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                        \
+      const int r = wm * WTM + tm * 32 + (lane & 31);                                          \
+      F##b[tm] = *reinterpret_cast<const bf16x8_t*>(sa_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
+    }                                                                                          \
+    _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                        \
+      const int r = nrow[tn] + (lane & 31);                                                    \
+      F##a[tn] = *reinterpret_cast<const bf16x8_t*>(sw_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
+    }                                                                                          \
+  } while (0)
 
+  constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
+  static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
+
+  // prologue: stages 0..NS-1 in flight (one per buffer), stage 0 landed,
+  // its first fragments read
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nk) MOE_ISSUE_STAGE(s, s);
+  if (NS <= nk) wait_vmcnt<(NS - 1) * (LA + LB)>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+  MOE_LOAD_FRAGS(f0, 0, 0);
+
+  // Steady state. Fragments of the next sub-step are read before the matrix
+  // ops of the current one. In the last sub-step of a stage its fragments
+  // are already in registers, so the wait for stage kt+1, the barrier, the
+  // issue of stage kt+NS into the buffer stage kt leaves free, and the reads
+  // of stage kt+1's first fragments all overlap that sub-step's matrix ops.
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the later stages' loads are pending
-    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * (LA + LB)>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // every wave's loads of stage kt are visible; stage kt-1 is free
-    if (kt + NS - 1 < nk) MOE_ISSUE_STAGE((kt + NS - 1) % NS, kt + NS - 1);
-    const char* sa = smem + (kt % NS) * STAGE;
-    const char* sw = sa + A_BYTES;
+    const int buf = kt % NS;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8_t bt[TM], aw[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int r = wm * WTM + tm * 32 + (lane & 31);
-        bt[tm] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((c ^ swz(r)) << 4));
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+        if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, buf, kk + 1);
+        else MOE_LOAD_FRAGS(f0, buf, kk + 1);
+      } else if (kt + 1 < nk) {
+        // issued so far: stages 0 .. min(kt+NS-1, nk-1); stage kt+1 must have landed
+        if (kt + NS - 1 < nk) wait_vmcnt<(NS - 2) * (LA + LB)>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // stage kt+1 visible to all; every wave is done reading stage kt
+        if (kt + NS < nk) MOE_ISSUE_STAGE(buf, kt + NS);
+        MOE_LOAD_FRAGS(f0, (kt + 1) % NS, 0);
       }
+      if (kk % 2 == 0) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int r = nrow[tn] + (lane & 31);
-        aw[tn] = *reinterpret_cast<const bf16x8_t*>(sw + r * ROWB + ((c ^ swz(r)) << 4));
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[tn], f0b[tm], acc[tn][tm], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
       }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[tn], bt[tm], acc[tn][tm], 0, 0, 0);
     }
   }
+#undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
   // ---- epilogues ----
@@ -326,33 +369,38 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE>
 hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const int64_t total = (int64_t)a.max_tiles * a.n_tiles;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-  grouped_gemm<BM, BN, WGM, WGN, NS, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
+  grouped_gemm<BM, BN, BK, WGM, WGN, NS, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   a.group_m = 8;
-  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 2, 2, 2, MODE>(a, stream);
-  if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 2, 2, 2, MODE>(a, stream);
-  if (cfg.bm == 128 && cfg.bn == 256) return launch_cfg<128, 256, 2, 2, 2, MODE>(a, stream);
+  // (token rows, weight rows, waves): the variants kept after sweeping tile
+  // shape, pipeline depth and wave layout on the workloads' shapes
+  if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE>(a, stream);
+  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE>(a, stream);
+  if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE>(a, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// Row tile from the mean number of rows per routed expert: big tiles reuse
+// each staged byte more, small tiles waste fewer pad rows.
 GemmCfg pick_gemm1_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E) {
   (void)H;
   (void)I;
   const int64_t live = n_slots < E ? n_slots : E;
   const int64_t rows_per_expert = live > 0 ? n_slots / live : 0;
-  if (rows_per_expert < 96) return GemmCfg{64, 128};
-  return GemmCfg{128, 128};
+  if (rows_per_expert >= 2048) return GemmCfg{256, 256};
+  if (rows_per_expert >= 96) return GemmCfg{128, 128};
+  return GemmCfg{64, 256};
 }
 
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm) {
@@ -360,7 +408,9 @@ GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm)
   (void)H;
   (void)I;
   (void)E;
-  return GemmCfg{bm, 128};
+  if (bm == 256) return GemmCfg{256, 256};
+  if (bm == 128) return GemmCfg{128, 128};
+  return GemmCfg{64, 256};
 }
 
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,

@@ -335,15 +335,15 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    void* stream) {
   int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  if (m_tile != 64 && m_tile != 128)
-    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64 and 128", m_tile);
+  if (m_tile != 64 && m_tile != 128 && m_tile != 256)
+    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128 and 256", m_tile);
   if (max_tiles < 0 || max_tiles > INT32_MAX)
     return set_error(MOE_ERR_INVALID_ARG, "max_tiles=%lld", (long long)max_tiles);
   if (T == 0 || max_tiles == 0) return MOE_OK;
   if (!hidden || !w1 || !sorted || !tile_expert || !num_tiles || !act)
     return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
   hipError_t st = moe::launch_gemm1_silu(
-      moe::GemmCfg{m_tile, 128}, static_cast<const uint16_t*>(hidden),
+      moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256}, static_cast<const uint16_t*>(hidden),
       static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
       static_cast<uint16_t*>(act), static_cast<hipStream_t>(stream));
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
