@@ -5,38 +5,44 @@
 // This is the regime the metrale forward_k2 dispatch serves with separate
 // gate/up, silu/down and weighted-sum kernels per row pair; here two
 // launches do it for any small T:
-//   decode_gateup  one wave per (slot, i): streams the gate row i and the up
-//                  row I+i of the slot's expert (16-byte loads, 64 lanes over
-//                  consecutive chunks), reduces across the wave and stores
-//                  act[slot, i] = bf16(silu(g) * u);
-//   decode_down    one wave per (token, pair of output rows h): streams
-//                  w2[e_k, h, :] for every k of the token, with the token's
-//                  K activation rows held in registers, and writes
+//   decode_gateup  one wave per (slot, i pair): streams the gate rows i, i+1
+//                  and up rows I+i, I+i+1 of the slot's expert (16-byte loads,
+//                  64 lanes over consecutive chunks, all issued up front),
+//                  reduces across the wave and stores act = bf16(silu(g) * u);
+//   decode_down    one wave per (token, output row h): streams w2[e_k, h, :]
+//                  for every k of the token together with the token's K
+//                  activation rows, and writes
 //                  out[t, h] = sum_k w_k * (w2[e_k, h, :] . act[t*K+k, :]).
 // No atomics: each output element is produced by exactly one wave.
 #include "moe_internal.h"
+
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kDownRows = 2;    // output rows per wave in decode_down
 constexpr int kMaxDownIter = 32;  // 16-byte chunks per lane held in registers
 
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
-  float s = bf16lo(a.x) * bf16lo(b.x);
-  s = fmaf(bf16hi(a.x), bf16hi(b.x), s);
-  s = fmaf(bf16lo(a.y), bf16lo(b.y), s);
-  s = fmaf(bf16hi(a.y), bf16hi(b.y), s);
-  s = fmaf(bf16lo(a.z), bf16lo(b.z), s);
-  s = fmaf(bf16hi(a.z), bf16hi(b.z), s);
-  s = fmaf(bf16lo(a.w), bf16lo(b.w), s);
-  s = fmaf(bf16hi(a.w), bf16hi(b.w), s);
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
+
+__device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
+  float s = bf16lo(a[0]) * bf16lo(b[0]);
+  s = fmaf(bf16hi(a[0]), bf16hi(b[0]), s);
+  s = fmaf(bf16lo(a[1]), bf16lo(b[1]), s);
+  s = fmaf(bf16hi(a[1]), bf16hi(b[1]), s);
+  s = fmaf(bf16lo(a[2]), bf16lo(b[2]), s);
+  s = fmaf(bf16hi(a[2]), bf16hi(b[2]), s);
+  s = fmaf(bf16lo(a[3]), bf16lo(b[3]), s);
+  s = fmaf(bf16hi(a[3]), bf16hi(b[3]), s);
   return s;
+}
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  return dot8(u32x4_t{a.x, a.y, a.z, a.w}, u32x4_t{b.x, b.y, b.z, b.w});
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -45,83 +51,114 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One wave per (slot, IPW consecutive intermediate columns): the IPW gate
+// rows and the IPW up rows of H bf16 each. NC = 16-byte chunks per lane per
+// row; every load of the wave is issued before the first use.
+template <int NC, int IPW>
 __global__ __launch_bounds__(kThreads) void decode_gateup(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ topk_ids, int64_t H, int64_t I, int32_t E, int32_t K,
     uint16_t* __restrict__ act) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t i0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * IPW;
   const int64_t f = blockIdx.y;
-  if (i >= I) return;
+  if (i0 >= I) return;
   const int32_t e = topk_ids[f];
   if (e < 0 || e >= E) {
-    if (lane == 0) act[f * I + i] = 0;
+    if (lane < IPW && i0 + lane < I) act[f * I + i0 + lane] = 0;
     return;
   }
   const int64_t t = f / K;
-  const uint4* x = reinterpret_cast<const uint4*>(hidden + t * H);
-  const uint4* wg = reinterpret_cast<const uint4*>(w1 + ((int64_t)e * 2 * I + i) * H);
-  const uint4* wu = reinterpret_cast<const uint4*>(w1 + ((int64_t)e * 2 * I + I + i) * H);
   const int64_t nc = H / 8;
-  float g = 0.f, u = 0.f;
-  for (int64_t c = lane; c < nc; c += 64) {
-    const uint4 xv = x[c];
-    g += dot8(wg[c], xv);
-    u += dot8(wu[c], xv);
+  // buffer loads: offsets past the end read zeros (no branches, no scratch)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(hidden + t * H), (short)0, (int)(H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w1 + (int64_t)e * 2 * I * H), (short)0, (int)(2 * I * H * 2), 0x00020000);
+  u32x4_t wv[2 * IPW][NC], xv[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int64_t c = lane + 64 * j;
+    const bool ok = c < nc;
+#pragma unroll
+    for (int r = 0; r < IPW; ++r) {
+      const bool okr = ok && (i0 + r < I);
+      const uint32_t og = okr ? (uint32_t)(((i0 + r) * H + c * 8) * 2) : kOutOfRange;
+      const uint32_t ou = okr ? (uint32_t)(((I + i0 + r) * H + c * 8) * 2) : kOutOfRange;
+      wv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, og, 0, 0);
+      wv[IPW + r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ou, 0, 0);
+    }
+    xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? (uint32_t)(c * 16) : kOutOfRange, 0, 0);
   }
-  g = wave_sum(g);
-  u = wave_sum(u);
-  if (lane == 0) {
-    const float a = g / (1.0f + __expf(-g)) * u;
-    const __bf16 b = (__bf16)a;  // round to nearest even
-    act[f * I + i] = __builtin_bit_cast(uint16_t, b);
+  float s[2 * IPW];
+#pragma unroll
+  for (int r = 0; r < 2 * IPW; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int r = 0; r < 2 * IPW; ++r) s[r] += dot8(wv[r][j], xv[j]);
+#pragma unroll
+  for (int r = 0; r < 2 * IPW; ++r) s[r] = wave_sum(s[r]);
+#pragma unroll
+  for (int r = 0; r < IPW; ++r) {
+    if (lane == r && i0 + r < I) {
+      const float g = s[r], u = s[IPW + r];
+      const float a = g / (1.0f + __expf(-g)) * u;
+      const __bf16 b = (__bf16)a;  // round to nearest even
+      act[f * I + i0 + r] = __builtin_bit_cast(uint16_t, b);
+    }
   }
 }
 
+// One wave per (token, output row h): streams w2[e_k, h, :] for every k of
+// the token. J = 16-byte chunks per lane over the K activation rows.
 template <int J>
 __global__ __launch_bounds__(kThreads) void decode_down(
     const uint16_t* __restrict__ w2, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ topk_ids, const uint16_t* __restrict__ act, int64_t H,
     int64_t I, int32_t E, int32_t K, float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t h0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kDownRows;
+  const int64_t h = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t t = blockIdx.y;
-  if (h0 >= H) return;
+  if (h >= H) return;
   const int64_t cpr = I / 8;   // 16-byte chunks per row
   const int64_t nq = K * cpr;  // chunks over the token's K activation rows
-  uint4 av[J];
-  const uint4* wp[J];  // chunk of w2[e_k, 0, :]; row h adds h * I
+  // row h of each chosen expert's w2 and the token's activation rows; a
+  // dropped slot or a lane past the end loads from a valid address and its
+  // product is discarded (no branches around the loads)
+  const int32_t cpr32 = (int32_t)cpr, nq32 = (int32_t)nq;
+  const uint4* w2v = reinterpret_cast<const uint4*>(w2);
+  const uint4* av_base = reinterpret_cast<const uint4*>(act + t * K * I);
+  uint4 wv[J], av[J];
   float wk[J];
+  bool okj[J];
+  int32_t ej[J], qj[J], cj[J];
+  // first every routing lookup, then every weight/activation load, so the
+  // wave has all its row loads in flight at once
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int64_t q = lane + 64 * j;
-    wp[j] = nullptr;
-    wk[j] = 0.f;
-    av[j] = make_uint4(0, 0, 0, 0);
-    if (q < nq) {
-      const int64_t k = q / cpr;
-      const int64_t c = q - k * cpr;
-      const int32_t e = topk_ids[t * K + k];
-      if (e >= 0 && e < E) {
-        wp[j] = reinterpret_cast<const uint4*>(w2 + (int64_t)e * H * I) + c;
-        wk[j] = topk_weights[t * K + k];
-        av[j] = reinterpret_cast<const uint4*>(act + (t * K + k) * I)[c];
-      }
-    }
+    // 32-bit index math (a 64-bit division would branch per chunk)
+    const int32_t q = lane + 64 * j;
+    const int32_t k = q < nq32 ? (int32_t)((uint32_t)q / (uint32_t)cpr32) : K - 1;  // clamped
+    qj[j] = q;
+    cj[j] = q - k * cpr32;
+    ej[j] = topk_ids[t * K + k];
+    wk[j] = topk_weights[t * K + k];
   }
-  const int64_t row_stride = I / 8;  // in uint4
 #pragma unroll
-  for (int r = 0; r < kDownRows; ++r) {
-    const int64_t h = h0 + r;
-    if (h >= H) break;
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (wp[j]) s = fmaf(wk[j], dot8(wp[j][h * row_stride], av[j]), s);
-    }
-    s = wave_sum(s);
-    if (lane == 0) out[t * H + h] = s;
+  for (int j = 0; j < J; ++j) {
+    okj[j] = qj[j] < nq32 && ej[j] >= 0 && ej[j] < E;
+    wv[j] = w2v[okj[j] ? ((int64_t)ej[j] * H + h) * cpr + cj[j] : 0];
+    av[j] = av_base[okj[j] ? qj[j] : 0];
   }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const float d = wk[j] * dot8(wv[j], av[j]);
+    s += okj[j] ? d : 0.f;
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[t * H + h] = s;
 }
 
 }  // namespace
@@ -131,15 +168,22 @@ hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint1
                          int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,
                          float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int64_t iters = (K * (I / 8) + 63) / 64;
-  if (iters > kMaxDownIter) return hipErrorInvalidValue;
-  dim3 g1((unsigned)((I + kWaves - 1) / kWaves), (unsigned)(T * K));
-  decode_gateup<<<g1, kThreads, 0, stream>>>(hidden, w1, topk_ids, H, I, (int32_t)E,
-                                             (int32_t)K, act);
+  const int64_t nc = (H / 8 + 63) / 64;           // chunks per lane per gate/up row
+  const int64_t iters = (K * (I / 8) + 63) / 64;  // chunks per lane in the down kernel
+  if (nc > 16 || iters > kMaxDownIter) return hipErrorInvalidValue;
+  constexpr int kIPW = 1;  // one gate/up column pair per wave measured fastest
+  dim3 g1((unsigned)((I + kIPW * kWaves - 1) / (kIPW * kWaves)), (unsigned)(T * K));
+#define MOE_GATEUP(NN) \
+  decode_gateup<NN, kIPW><<<g1, kThreads, 0, stream>>>(hidden, w1, topk_ids, H, I, (int32_t)E, (int32_t)K, act)
+  if (nc <= 1) MOE_GATEUP(1);
+  else if (nc <= 2) MOE_GATEUP(2);
+  else if (nc <= 4) MOE_GATEUP(4);
+  else if (nc <= 8) MOE_GATEUP(8);
+  else MOE_GATEUP(16);
+#undef MOE_GATEUP
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
-  const int64_t rows_per_block = (int64_t)kWaves * kDownRows;
-  dim3 g2((unsigned)((H + rows_per_block - 1) / rows_per_block), (unsigned)T);
+  dim3 g2((unsigned)((H + kWaves - 1) / kWaves), (unsigned)T);
 #define MOE_DOWN(JJ)                                                                     \
   decode_down<JJ><<<g2, kThreads, 0, stream>>>(w2, topk_weights, topk_ids, act, H, I, \
                                                (int32_t)E, (int32_t)K, out)
@@ -154,6 +198,8 @@ hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint1
 }
 
 // Largest K * I the decode path can hold in registers.
-bool decode_supported(int64_t I, int64_t K) { return K * (I / 8) <= 64 * kMaxDownIter; }
+bool decode_supported(int64_t H, int64_t I, int64_t K) {
+  return K * (I / 8) <= 64 * kMaxDownIter && H / 8 <= 64 * 16;
+}
 
 }  // namespace moe

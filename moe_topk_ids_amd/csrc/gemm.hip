@@ -43,6 +43,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 
 enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2 };
@@ -122,7 +123,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;  // token rows per wave
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 1, "tile too small");
   static_assert(MODE != kGateUpSilu || (TN % 2 == 0), "gate/up pairing needs even TN");
   static_assert(NS >= 2, "at least two stages");
+  static_assert(P == 0 || NS == 2, "register staging uses a two-buffer LDS ring");
 
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
@@ -173,14 +175,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   // load j of this wave covers staged rows RPL*g .. RPL*g+RPL-1 (g = wave*L
   // + j); lane -> row RPL*g + lane/CPR, physical chunk lane%CPR, logical
   // chunk (lane%CPR) ^ swz(row): the XOR layout is applied on the global side.
-  int32x4_t rsrc_a, rsrc_b;
   uint32_t aoff[LA], boff[LB];
-  if (MODE == kGateUpSilu) {
-    rsrc_a = make_rsrc(args.a, args.a_bytes);
-  } else {
-    rsrc_a = make_rsrc(args.a + m0 * kdim, (uint32_t)(BM * kdim * 2));
-  }
-  rsrc_b = make_rsrc(args.w + (int64_t)e * args.w_expert_stride, (uint32_t)(args.w_expert_stride * 2));
+  const uint16_t* a_base = MODE == kGateUpSilu ? args.a : args.a + m0 * kdim;
+  const uint32_t a_num = MODE == kGateUpSilu ? args.a_bytes : (uint32_t)(BM * kdim * 2);
+  const uint16_t* b_base = args.w + (int64_t)e * args.w_expert_stride;
+  const uint32_t b_num = (uint32_t)(args.w_expert_stride * 2);
+  const int32x4_t rsrc_a = make_rsrc(a_base, a_num);
+  const int32x4_t rsrc_b = make_rsrc(b_base, b_num);
+  const __amdgpu_buffer_rsrc_t brsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_num, 0x00020000);
+  const __amdgpu_buffer_rsrc_t brsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_num, 0x00020000);
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     const int r = RPL * (wave * LA + j) + lane / CPR;
@@ -261,6 +266,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
   static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
 
+  if constexpr (P == 0) {
   // prologue: stages 0..NS-1 in flight (one per buffer), stage 0 landed,
   // its first fragments read
 #pragma unroll
@@ -306,6 +312,73 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
             acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
       }
     }
+  }
+  } else {
+    // Register staging: stage s is loaded into register set s % P, P stages
+    // ahead of its use, and written to LDS buffer s % 2 one stage ahead. The
+    // VGPR file holds several times more bytes in flight than LDS could.
+    u32x4_t R[P][LA + LB];
+#define MOE_GLOAD(set, kt)                                                                     \
+  do {                                                                                         \
+    const uint32_t kb_ = (uint32_t)(kt) * ROWB;                                                \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                            \
+        R[set][j] = __builtin_amdgcn_raw_buffer_load_b128(brsrc_a, aoff[j] + kb_, 0, 0);       \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                            \
+        R[set][LA + j] = __builtin_amdgcn_raw_buffer_load_b128(brsrc_b, boff[j] + kb_, 0, 0);  \
+  } while (0)
+#define MOE_SSTORE(set, buf)                                                                   \
+  do {                                                                                         \
+    char* sb_ = smem + (buf) * STAGE + lane * 16;                                              \
+    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                            \
+        *reinterpret_cast<u32x4_t*>(sb_ + (wave * LA + j) * 1024) = R[set][j];                 \
+    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                            \
+        *reinterpret_cast<u32x4_t*>(sb_ + A_BYTES + (wave * LB + j) * 1024) = R[set][LA + j];  \
+  } while (0)
+#pragma unroll
+    for (int s2 = 0; s2 < P; ++s2)
+      if (s2 < nk) MOE_GLOAD(s2, s2);
+    MOE_SSTORE(0, 0);
+    if (P < nk) MOE_GLOAD(0, P);
+    __syncthreads();
+    bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+    MOE_LOAD_FRAGS(f0, 0, 0);
+    for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const int kt = kt0 + u;
+        if (kt >= nk) break;
+        if (kt + 1 < nk) {
+          // buffer (kt+1)&1 was last read in stage kt-1, before its final barrier
+          MOE_SSTORE((u + 1) % P, (kt + 1) & 1);
+          if (kt + 1 + P < nk) MOE_GLOAD((u + 1) % P, kt + 1 + P);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) {
+            if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, kt & 1, kk + 1);
+            else MOE_LOAD_FRAGS(f0, kt & 1, kk + 1);
+          } else if (kt + 1 < nk) {
+            __syncthreads();  // stage kt+1 written by all; stage kt read by all
+            MOE_LOAD_FRAGS(f0, (kt + 1) & 1, 0);
+          }
+          if (kk % 2 == 0) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+              for (int tm = 0; tm < TM; ++tm)
+                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[tn], f0b[tm], acc[tn][tm], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+              for (int tm = 0; tm < TM; ++tm)
+                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
+          }
+        }
+      }
+    }
+#undef MOE_GLOAD
+#undef MOE_SSTORE
   }
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
@@ -369,12 +442,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
 hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const int64_t total = (int64_t)a.max_tiles * a.n_tiles;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-  grouped_gemm<BM, BN, BK, WGM, WGN, NS, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
+  grouped_gemm<BM, BN, BK, WGM, WGN, NS, P, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -383,9 +456,9 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   a.group_m = 8;
   // (token rows, weight rows, waves): the variants kept after sweeping tile
   // shape, pipeline depth and wave layout on the workloads' shapes
-  if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE>(a, stream);
-  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE>(a, stream);
-  if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE>(a, stream);
+  if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, 0, MODE>(a, stream);
+  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, 0, MODE>(a, stream);
+  if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, 0, MODE>(a, stream);
   return hipErrorInvalidValue;
 }
 

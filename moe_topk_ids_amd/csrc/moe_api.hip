@@ -68,8 +68,8 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   return MOE_OK;
 }
 
-bool use_decode(int64_t T, int64_t I, int64_t K, uint32_t flags) {
-  if (!moe::decode_supported(I, K)) return false;
+bool use_decode(int64_t T, int64_t H, int64_t I, int64_t K, uint32_t flags) {
+  if (!moe::decode_supported(H, I, K)) return false;
   if (flags & MOE_FLAG_FORCE_DECODE) return true;
   if (flags & MOE_FLAG_FORCE_GROUPED) return false;
   return T * K <= kDecodeMaxSlots;
@@ -94,7 +94,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
     return at;
   };
   L.err = take(sizeof(int32_t));
-  if (use_decode(T, I, K, flags)) {
+  if (use_decode(T, H, I, K, flags)) {
     L.decode = true;
     L.act = take((size_t)n * I * 2);
     L.total = p;
@@ -198,7 +198,7 @@ int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
 int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   const int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  return use_decode(T, I, K, flags) ? 1 : 0;
+  return use_decode(T, H, I, K, flags) ? 1 : 0;
 }
 
 int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,

@@ -67,7 +67,7 @@ hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
 hipError_t launch_validate_ids(const int32_t* ids, int64_t T, int64_t K, int64_t E,
                                int32_t* err_flag, hipStream_t stream);
 
-bool decode_supported(int64_t I, int64_t K);
+bool decode_supported(int64_t H, int64_t I, int64_t K);
 
 hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                          const float* topk_weights, const int32_t* topk_ids, int64_t T,
