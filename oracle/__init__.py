@@ -45,6 +45,8 @@ def _load():
     lib.oracle_moe_forward_f64.restype = None
     lib.oracle_slot_act_bf16.argtypes = [p, p, p, i64, i64, i64, i64, i64, p]
     lib.oracle_slot_act_bf16.restype = None
+    lib.oracle_topk_softmax.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p]
+    lib.oracle_topk_softmax.restype = None
     lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
     lib.oracle_bf16_to_f32.argtypes = [p, p, i64]
     _lib = lib
@@ -128,6 +130,17 @@ def slot_act_bf16(x, w1, topk_ids) -> np.ndarray:
     out = np.zeros((T * K, I), np.uint16)
     lib.oracle_slot_act_bf16(_ptr(x), _ptr(w1), _ptr(ids), T, H, I, E, K, _ptr(out))
     return out
+
+
+def topk_softmax(logits, K: int, renormalize: bool = True):
+    """Router oracle: (weights fp32 [T,K], ids int32 [T,K]) from fp32 logits [T,E]."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    w = np.zeros((T, K), np.float32)
+    ids = np.zeros((T, K), np.int32)
+    lib.oracle_topk_softmax(_ptr(logits), T, E, K, 1 if renormalize else 0, _ptr(w), _ptr(ids))
+    return w, ids
 
 
 def f32_to_bf16(a: np.ndarray) -> np.ndarray:

@@ -264,3 +264,56 @@ void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_
     free(act);
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* Router: softmax -> top-K -> renormalise                            */
+/* ------------------------------------------------------------------ */
+
+/*
+ * For each token t (logits fp32 [T,E]):
+ *   m = max_e logits[t,e];  p[e] = exp(logits[t,e] - m) / sum_e' exp(logits[t,e'] - m)
+ *   ([atrex-009] Input Generation: softmax over experts; [tpu-ref] ref_moe and
+ *   get_top_k in tpu-inference kernel.py apply softmax to the gating logits).
+ *   K rounds of: pick the largest remaining expert, ties to the lowest id
+ *   (get_top_k's argmax takes the first index), remove it.
+ *   Selection compares the fp32 logits: softmax is strictly increasing, so
+ *   this is the order of the exact probabilities, and it does not depend on
+ *   how exp() rounds.
+ *   ids[t,k] = chosen expert k (descending); weights[t,k] = p of that expert,
+ *   divided, if renormalize, by the sum of the K chosen p added in k order
+ *   (get_top_k's renormalisation; [atrex-009] divides by the sum of the top
+ *   values). All arithmetic fp32, exp() from libm, sums in ascending order.
+ */
+void oracle_topk_softmax(const float* logits, int64_t T, int64_t E, int64_t K, int renormalize,
+                         float* weights, int32_t* ids) {
+#pragma omp parallel
+  {
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const float* l = logits + t * E;
+      float m = l[0];
+      for (int64_t e = 1; e < E; ++e)
+        if (l[e] > m) m = l[e];
+      float denom = 0.0f;
+      for (int64_t e = 0; e < E; ++e) denom = denom + expf(l[e] - m);
+      for (int64_t e = 0; e < E; ++e) taken[e] = 0;
+      float chosen_sum = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+          if (taken[e]) continue;
+          if (best < 0 || l[e] > l[best]) best = e; /* strict: ties keep the lower id */
+        }
+        taken[best] = 1;
+        ids[t * K + k] = (int32_t)best;
+        const float p = expf(l[best] - m) / denom;
+        weights[t * K + k] = p;
+        chosen_sum = chosen_sum + p;
+      }
+      if (renormalize)
+        for (int64_t k = 0; k < K; ++k) weights[t * K + k] = weights[t * K + k] / chosen_sum;
+    }
+    free(taken);
+  }
+}
