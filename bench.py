@@ -96,6 +96,42 @@ def cpu_baseline(d: dict, s, budget_s: float):
             "us_per_call_extrapolated": dt / n * s.T * 1e6}
 
 
+def bench_router(args, s):
+    """The router (moe_topk_softmax) alone on the workload's router logits."""
+    d = make_inputs(s.T, 128, 128, s.E, s.K, seed=0)  # only the logits are used
+    logits = d["router_logits"].cuda()
+    w = torch.empty((s.T, s.K), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s.T, s.K), dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        moe.moe_topk_softmax(logits, s.K, topk_weights=w, topk_ids=ids)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        moe.moe_topk_softmax(logits, s.K, topk_weights=w, topk_ids=ids)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = (t1 - t0) * 1e6 / args.steps
+    us_ev = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    nbytes = s.T * s.E * 4 + s.T * s.K * 8
+    print(json.dumps({
+        "metric": "router softmax->top-k->renormalise GB/s and µs/call", "value": nbytes / us / 1e3,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": us / 1e3, "us_per_call": us, "us_per_call_events": us_ev,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded fp32 N(0,1) router logits)",
+        "config": {"workload": f"{s.name} router: T={s.T} E={s.E} top_k={s.K}", "T": s.T,
+                   "E": s.E, "top_k": s.K},
+        "roofline": {"bound": "hbm", "kernel": "topk_softmax_kernel", "achieved": nbytes / us_ev / 1e3,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": nbytes / us_ev / 1e3 / PEAK_HBM_GBS,
+                     "algorithmic_bytes": nbytes, "avg_launch_us": us_ev, "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +142,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one weight copy every step")
+    ap.add_argument("--stage", default="forward", choices=["forward", "router"],
+                    help="forward: the fused MoE forward (default); router: softmax/top-k alone")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -117,6 +155,8 @@ def main():
     moe.load_library()
 
     s = SHAPES[args.workload]
+    if args.stage == "router":
+        return bench_router(args, s)
     flags = PATHS[args.path]
     log(f"[bench] workload {s} path {args.path}: generating inputs")
     d = make_inputs(s.T, s.H, s.I, s.E, s.K, seed=0)

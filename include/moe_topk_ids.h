@@ -154,6 +154,22 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int32_t m_tile,
                    int64_t max_tiles, void* act, void* stream);
 
+/*
+ * The router that produces topk_weights / topk_ids from fp32 router logits
+ * [T,E] (the softmax-then-top-k step of the atrex-bench #009 "Input
+ * Generation" section, tpu-inference get_top_k, metrale
+ * moe_topk_softmax_batched):
+ *   p[e] = softmax over the E logits of the token (fp32);
+ *   ids[t, 0..K-1] = the K experts with the largest logits, in descending
+ *       order, ties to the lower id (the same order as the probabilities);
+ *   weights[t,k] = p[ids[t,k]], divided by sum_k p[ids[t,k]] if
+ *       `renormalize` is non-zero.
+ * logits fp32 [T,E] row-major (finite values); weights fp32 [T,K]; ids int32
+ * [T,K]. 1 <= K <= min(E, 32), E <= 1024. Asynchronous on `stream`.
+ */
+int moe_topk_softmax(const float* router_logits, int64_t T, int64_t E, int64_t K,
+                     int renormalize, float* topk_weights, int32_t* topk_ids, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -65,6 +65,8 @@ def load_library():
     lib.moe_route_scratch_bytes.restype = sz
     lib.moe_gemm1_silu.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, i64, p, p]
     lib.moe_gemm1_silu.restype = ctypes.c_int
+    lib.moe_topk_softmax.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p, p]
+    lib.moe_topk_softmax.restype = ctypes.c_int
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_release.argtypes = []
@@ -218,6 +220,28 @@ def moe_gemm1_silu(hidden_states, w1, route: dict, K: int, m_tile: int, act=None
                               _ptr(route["tile_expert"]), _ptr(route["num_tiles"]), T, H, I, E, K,
                               m_tile, cap // m_tile, _ptr(act), _stream(stream)))
     return act
+
+
+def moe_topk_softmax(router_logits, top_k: int, renormalize: bool = True, topk_weights=None,
+                     topk_ids=None, stream=None):
+    """(topk_weights fp32 [T,K], topk_ids int32 [T,K]) from fp32 logits [T,E]."""
+    import torch
+
+    lib = load_library()
+    _need(router_logits, "router_logits", torch.float32, 2)
+    T, E = router_logits.shape
+    dev = router_logits.device
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    if tuple(topk_weights.shape) != (T, top_k) or tuple(topk_ids.shape) != (T, top_k):
+        raise ValueError("outputs must be [T, top_k]")
+    _check(lib.moe_topk_softmax(_ptr(router_logits), T, E, top_k, 1 if renormalize else 0,
+                                _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
+    return topk_weights, topk_ids
 
 
 def moe_release():

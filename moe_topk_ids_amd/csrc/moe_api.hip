@@ -349,6 +349,22 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
 }
 
+int moe_topk_softmax(const float* router_logits, int64_t T, int64_t E, int64_t K,
+                     int renormalize, float* topk_weights, int32_t* topk_ids, void* stream) {
+  if (T < 0 || E <= 0 || K <= 0 || K > E)
+    return set_error(MOE_ERR_INVALID_ARG, "bad sizes T=%lld E=%lld K=%lld", (long long)T,
+                     (long long)E, (long long)K);
+  if (E > moe::kMaxExperts || K > 32)
+    return set_error(MOE_ERR_UNSUPPORTED, "E=%lld (max %d) K=%lld (max 32)", (long long)E,
+                     moe::kMaxExperts, (long long)K);
+  if (T == 0) return MOE_OK;
+  if (!router_logits || !topk_weights || !topk_ids)
+    return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
+  hipError_t st = moe::launch_topk_softmax(router_logits, T, E, K, renormalize != 0, topk_weights,
+                                           topk_ids, static_cast<hipStream_t>(stream));
+  return st == hipSuccess ? MOE_OK : hip_error("moe_topk_softmax", st);
+}
+
 void moe_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int cur = 0;

@@ -69,6 +69,10 @@ hipError_t launch_validate_ids(const int32_t* ids, int64_t T, int64_t K, int64_t
 
 bool decode_supported(int64_t H, int64_t I, int64_t K);
 
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int64_t K,
+                               bool renormalize, float* weights, int32_t* ids,
+                               hipStream_t stream);
+
 hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                          const float* topk_weights, const int32_t* topk_ids, int64_t T,
                          int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,

@@ -30,7 +30,7 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
-              "moe_uses_decode_path"):
+              "moe_uses_decode_path", "moe_topk_softmax"):
         assert n in names
 
 
@@ -66,6 +66,15 @@ def test_route_argument_validation(lib):
     assert lib.moe_route(p, 4, 2, 8, 48, p, p, p, p, p, p, 1000, p, p) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(p, 4, 2, 8, 64, p, p, p, p, p, p, 10, p, p) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_gemm1_silu(p, p, p, p, p, 4, 128, 128, 8, 2, 32, 1, p, p) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_router_argument_validation(lib):
+    p = ctypes.c_void_p(0)
+    assert lib.moe_topk_softmax(p, 4, 8, 9, 1, p, p, p) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_topk_softmax(p, 4, 2000, 2, 1, p, p, p) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_topk_softmax(p, 4, 64, 40, 1, p, p, p) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_topk_softmax(p, 0, 8, 2, 1, p, p, p) == moe.MOE_OK
+    assert lib.moe_topk_softmax(p, 3, 8, 2, 1, p, p, p) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_and_tile_queries(lib):
