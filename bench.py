@@ -142,8 +142,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one weight copy every step")
-    ap.add_argument("--stage", default="forward", choices=["forward", "router"],
-                    help="forward: the fused MoE forward (default); router: softmax/top-k alone")
+    ap.add_argument("--stage", default="forward", choices=["forward", "router", "copy"],
+                    help="forward: the fused MoE forward (default); router: softmax/top-k "
+                         "alone; copy: a plain 512 MiB device copy, the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -157,6 +159,16 @@ def main():
     s = SHAPES[args.workload]
     if args.stage == "router":
         return bench_router(args, s)
+    if args.stage == "copy":
+        n = 512 * 2 ** 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"stage": "copy", "bytes_read": n, "bytes_written": n,
+                          "launches": max(args.steps, 1)}), flush=True)
+        return None
     flags = PATHS[args.path]
     log(f"[bench] workload {s} path {args.path}: generating inputs")
     d = make_inputs(s.T, s.H, s.I, s.E, s.K, seed=0)
