@@ -29,7 +29,7 @@ import numpy as np
 import torch
 
 import moe_topk_ids_amd as moe
-from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_inputs
+from moe_topk_ids_amd.inputs import SHAPES, SHAPES_TABLE, bf16_bits, make_inputs
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 METRIC = "fused-MoE bf16 TFLOP/s and µs/call per shape; % of MFMA/HBM roofline at 1 GPU"
@@ -132,6 +132,99 @@ def bench_router(args, s):
     }), flush=True)
 
 
+def _time_forward(dev, copies, w1s, w2s, out, flags, steps, warmup):
+    """us per forward, rotating over the weight copies; HIP events."""
+    def step(i):
+        moe.moe_forward(dev["hidden_states"], w1s[i % copies], w2s[i % copies],
+                        dev["topk_weights"], dev["topk_ids"], out=out, flags=flags)
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / steps
+
+
+def _group_inputs(H, I, E, K, T_max):
+    d = make_inputs(T_max, H, I, E, K, seed=0)
+    return {k: v.cuda() for k, v in d.items()}
+
+
+def _copies_for(ids_cpu, H, I):
+    touched = len(np.unique(ids_cpu.numpy()))
+    return max(1, min(8, -(-512 * 2 ** 20 // (touched * 3 * H * I * 2))))
+
+
+def bench_table(args):
+    """Every row of the shapes table: us/call and TFLOP/s next to the page's
+    T_SOL and T_Prod (measured there on its "XPU-A" hardware)."""
+    groups = {}
+    for row in SHAPES_TABLE:
+        groups.setdefault(row[1:5], []).append(row)
+    results = []
+    for (H, I, E, K), rows in groups.items():
+        T_max = max(r[0] for r in rows)
+        log(f"[table] H={H} I={I} E={E} K={K}: generating inputs for T={T_max}")
+        dev = _group_inputs(H, I, E, K, T_max)
+        for (T, _, _, _, _, t_sol, t_prod) in rows:
+            sub = {k: (v[:T].contiguous() if k in ("hidden_states", "topk_weights", "topk_ids")
+                       else v) for k, v in dev.items()}
+            copies = _copies_for(sub["topk_ids"].cpu(), H, I)
+            w1s = [sub["w1"]] + [sub["w1"].clone() for _ in range(copies - 1)]
+            w2s = [sub["w2"]] + [sub["w2"].clone() for _ in range(copies - 1)]
+            out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            flop = 6.0 * T * K * H * I
+            est = max(flop / 5e14 * 1e6, 20.0)
+            steps = int(max(5, min(100, 3e5 / est)))
+            us = _time_forward(sub, copies, w1s, w2s, out, None, steps, 3)
+            decode = moe.moe_uses_decode_path(T, H, I, E, K)
+            rec = {"T": T, "H": H, "I": I, "E": E, "top_k": K, "us_per_call": us,
+                   "tflops": flop / us / 1e6, "path": "decode" if decode else "grouped",
+                   "page_t_sol_us": t_sol, "page_t_prod_us": t_prod,
+                   "speedup_vs_page_t_prod": t_prod / us}
+            results.append(rec)
+            log(f"[table] T={T:6d} H={H} I={I} E={E:3d} K={K}: {us:9.1f} us {rec['tflops']:7.1f} "
+                f"TFLOP/s  page T_Prod {t_prod:8.1f} us  x{t_prod / us:.2f}")
+            del w1s, w2s, out
+        del dev
+        torch.cuda.empty_cache()
+    print(json.dumps({"stage": "table", "rows": results}), flush=True)
+    return None
+
+
+def bench_small_t(args):
+    """Crossover of the weight-streaming decode path and the grouped path."""
+    results = []
+    for (H, I, E, K) in ((2048, 768, 128, 8), (2048, 2048, 8, 2), (4096, 384, 128, 8)):
+        dev = _group_inputs(H, I, E, K, 64)
+        for T in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64):
+            sub = {k: (v[:T].contiguous() if k in ("hidden_states", "topk_weights", "topk_ids")
+                       else v) for k, v in dev.items()}
+            copies = _copies_for(sub["topk_ids"].cpu(), H, I)
+            w1s = [sub["w1"]] + [sub["w1"].clone() for _ in range(copies - 1)]
+            w2s = [sub["w2"]] + [sub["w2"].clone() for _ in range(copies - 1)]
+            out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            row = {"T": T, "H": H, "I": I, "E": E, "top_k": K}
+            for name, fl in (("decode", moe.FLAG_FORCE_DECODE), ("grouped", moe.FLAG_FORCE_GROUPED)):
+                if name == "decode" and not moe.moe_uses_decode_path(T, H, I, E, K, fl):
+                    continue
+                row[name + "_us"] = _time_forward(sub, copies, w1s, w2s, out, fl, 50, 5)
+            row["default_path"] = "decode" if moe.moe_uses_decode_path(T, H, I, E, K) else "grouped"
+            results.append(row)
+            log(f"[small_t] {row}")
+            del w1s, w2s
+        del dev
+        torch.cuda.empty_cache()
+    print(json.dumps({"stage": "small_t", "rows": results}), flush=True)
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,10 +235,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one weight copy every step")
-    ap.add_argument("--stage", default="forward", choices=["forward", "router", "copy"],
+    ap.add_argument("--stage", default="forward",
+                    choices=["forward", "router", "copy", "table", "small_t"],
                     help="forward: the fused MoE forward (default); router: softmax/top-k "
                          "alone; copy: a plain 512 MiB device copy, the reference for "
-                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes; "
+                         "table: every row of the atrex-bench #009 shapes table; small_t: "
+                         "decode path vs grouped path for T = 1..64")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -159,6 +255,10 @@ def main():
     s = SHAPES[args.workload]
     if args.stage == "router":
         return bench_router(args, s)
+    if args.stage == "table":
+        return bench_table(args)
+    if args.stage == "small_t":
+        return bench_small_t(args)
     if args.stage == "copy":
         n = 512 * 2 ** 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -35,8 +36,12 @@ int hip_error(const char* what, hipError_t st) {
   return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(st));
 }
 
-// Token-slot count above which the grouped path is used.
-constexpr int64_t kDecodeMaxSlots = 16;
+// The weight-streaming path reads each routed slot's expert weights on its
+// own; the grouped path reads each routed expert once but has a fixed cost
+// (routing, sparse tiles). Measured crossover: T*K of about E + 16 slots
+// (24 at E=8/top-2, ~144 at E=128/top-8), capped for very many experts.
+constexpr int64_t kDecodeSlotsOverE = 16;
+constexpr int64_t kDecodeMaxSlots = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -68,11 +73,11 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   return MOE_OK;
 }
 
-bool use_decode(int64_t T, int64_t H, int64_t I, int64_t K, uint32_t flags) {
+bool use_decode(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   if (!moe::decode_supported(H, I, K)) return false;
   if (flags & MOE_FLAG_FORCE_DECODE) return true;
   if (flags & MOE_FLAG_FORCE_GROUPED) return false;
-  return T * K <= kDecodeMaxSlots;
+  return T * K <= std::min<int64_t>(E + kDecodeSlotsOverE, kDecodeMaxSlots);
 }
 
 // Byte offsets of every buffer inside one workspace.
@@ -94,7 +99,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
     return at;
   };
   L.err = take(sizeof(int32_t));
-  if (use_decode(T, H, I, K, flags)) {
+  if (use_decode(T, H, I, E, K, flags)) {
     L.decode = true;
     L.act = take((size_t)n * I * 2);
     L.total = p;
@@ -198,7 +203,7 @@ int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
 int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   const int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  return use_decode(T, H, I, K, flags) ? 1 : 0;
+  return use_decode(T, H, I, E, K, flags) ? 1 : 0;
 }
 
 int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
