@@ -161,6 +161,10 @@ def _copies_for(ids_cpu, H, I):
     return max(1, min(8, -(-512 * 2 ** 20 // (touched * 3 * H * I * 2))))
 
 
+_PATH_NAMES = {moe.PATH_GROUPED: "grouped", moe.PATH_DECODE: "decode",
+               moe.PATH_SMALL_BATCH: "small_batch"}
+
+
 def bench_table(args):
     """Every row of the shapes table: us/call and TFLOP/s next to the page's
     T_SOL and T_Prod (measured there on its "XPU-A" hardware)."""
@@ -183,9 +187,8 @@ def bench_table(args):
             est = max(flop / 5e14 * 1e6, 20.0)
             steps = int(max(5, min(100, 3e5 / est)))
             us = _time_forward(sub, copies, w1s, w2s, out, None, steps, 3)
-            decode = moe.moe_uses_decode_path(T, H, I, E, K)
             rec = {"T": T, "H": H, "I": I, "E": E, "top_k": K, "us_per_call": us,
-                   "tflops": flop / us / 1e6, "path": "decode" if decode else "grouped",
+                   "tflops": flop / us / 1e6, "path": _PATH_NAMES[moe.moe_path(T, H, I, E, K)],
                    "page_t_sol_us": t_sol, "page_t_prod_us": t_prod,
                    "speedup_vs_page_t_prod": t_prod / us}
             results.append(rec)
@@ -199,11 +202,15 @@ def bench_table(args):
 
 
 def bench_small_t(args):
-    """Crossover of the weight-streaming decode path and the grouped path."""
+    """Crossover of the per-token and per-expert weight-streaming paths and
+    the grouped path."""
     results = []
-    for (H, I, E, K) in ((2048, 768, 128, 8), (2048, 2048, 8, 2), (4096, 384, 128, 8)):
-        dev = _group_inputs(H, I, E, K, 64)
-        for T in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64):
+    for (H, I, E, K) in ((2048, 768, 128, 8), (2048, 2048, 8, 2), (4096, 384, 128, 8),
+                         (4096, 4096, 8, 2)):
+        dev = _group_inputs(H, I, E, K, 512)
+        for T in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512):
+            if T * K > 1024:
+                continue
             sub = {k: (v[:T].contiguous() if k in ("hidden_states", "topk_weights", "topk_ids")
                        else v) for k, v in dev.items()}
             copies = _copies_for(sub["topk_ids"].cpu(), H, I)
@@ -211,11 +218,15 @@ def bench_small_t(args):
             w2s = [sub["w2"]] + [sub["w2"].clone() for _ in range(copies - 1)]
             out = torch.empty((T, H), dtype=torch.float32, device="cuda")
             row = {"T": T, "H": H, "I": I, "E": E, "top_k": K}
-            for name, fl in (("decode", moe.FLAG_FORCE_DECODE), ("grouped", moe.FLAG_FORCE_GROUPED)):
-                if name == "decode" and not moe.moe_uses_decode_path(T, H, I, E, K, fl):
+            for name, fl in (("decode", moe.FLAG_FORCE_DECODE),
+                             ("small_batch", moe.FLAG_FORCE_SMALL_BATCH),
+                             ("grouped", moe.FLAG_FORCE_GROUPED)):
+                if _PATH_NAMES[moe.moe_path(T, H, I, E, K, fl)] != name:
                     continue
-                row[name + "_us"] = _time_forward(sub, copies, w1s, w2s, out, fl, 50, 5)
-            row["default_path"] = "decode" if moe.moe_uses_decode_path(T, H, I, E, K) else "grouped"
+                if name == "decode" and T * K > 256:
+                    continue  # per-slot streaming: far off the pace by then
+                row[name + "_us"] = _time_forward(sub, copies, w1s, w2s, out, fl, 30, 3)
+            row["default_path"] = _PATH_NAMES[moe.moe_path(T, H, I, E, K)]
             results.append(row)
             log(f"[small_t] {row}")
             del w1s, w2s

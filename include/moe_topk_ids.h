@@ -67,13 +67,23 @@ extern "C" {
 #define MOE_FLAG_ATOMIC_COMBINE 1u
 /* Force the grouped (routing + two grouped GEMMs) path. */
 #define MOE_FLAG_FORCE_GROUPED 2u
-/* Force the small-batch weight-streaming path. */
+/* Force the per-token weight-streaming path (each slot streams its own
+ * expert's rows; meant for one or two tokens). */
 #define MOE_FLAG_FORCE_DECODE 4u
 /* Synchronise the stream after every stage and name the first stage whose
  * kernels failed in moe_last_error(). */
 #define MOE_FLAG_DEBUG_SYNC 8u
 /* Check ids on the device; see the preconditions above. Synchronises. */
 #define MOE_FLAG_VALIDATE_IDS 16u
+/* Force the expert-deduplicated small-batch path (each routed expert's rows
+ * streamed once for all slots routed to it; T*K <= 1024). */
+#define MOE_FLAG_FORCE_SMALL_BATCH 32u
+
+/* Paths, as returned by moe_path. A FORCE flag whose path does not support
+ * the sizes falls back to the grouped path. */
+#define MOE_PATH_GROUPED 0     /* routing + two grouped MFMA GEMMs + combine */
+#define MOE_PATH_DECODE 1      /* per-token weight streaming, two kernels */
+#define MOE_PATH_SMALL_BATCH 2 /* per-expert weight streaming + combine */
 
 /*
  * The fused forward: out = sum_k topk_weights[:,k] * Expert_{topk_ids[:,k]}(hidden).
@@ -111,10 +121,13 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K
  * forward's routing). Returns a negative MOE_ERR_* code on invalid sizes. */
 int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
 
-/* 1 if moe_forward_ex would take the small-batch weight-streaming path for
- * these sizes and flags, 0 if the grouped path, negative MOE_ERR_* on
- * invalid sizes. */
+/* 1 if moe_forward_ex would take the per-token weight-streaming path for
+ * these sizes and flags, 0 otherwise, negative MOE_ERR_* on invalid sizes. */
 int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
+
+/* The MOE_PATH_* moe_forward_ex takes for these sizes and flags, or a
+ * negative MOE_ERR_* code on invalid sizes. */
+int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
 
 /*
  * The routing step alone (the grouping that tpu-inference's start_a2a_scatter

@@ -24,6 +24,11 @@ FLAG_FORCE_GROUPED = 2
 FLAG_FORCE_DECODE = 4
 FLAG_DEBUG_SYNC = 8
 FLAG_VALIDATE_IDS = 16
+FLAG_FORCE_SMALL_BATCH = 32
+
+PATH_GROUPED = 0
+PATH_DECODE = 1
+PATH_SMALL_BATCH = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_topk_ids.so")
 
@@ -59,6 +64,8 @@ def load_library():
     lib.moe_m_tile.restype = i32
     lib.moe_uses_decode_path.argtypes = [i64, i64, i64, i64, i64, u32]
     lib.moe_uses_decode_path.restype = ctypes.c_int
+    lib.moe_path.argtypes = [i64, i64, i64, i64, i64, u32]
+    lib.moe_path.restype = ctypes.c_int
     lib.moe_route.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, i64, p, p]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route_scratch_bytes.argtypes = [i64, i64, i64]
@@ -167,6 +174,14 @@ def moe_uses_decode_path(T, H, I, E, K, flags=0) -> bool:
     if v < 0:
         _check(v)
     return bool(v)
+
+
+def moe_path(T, H, I, E, K, flags=0) -> int:
+    """PATH_GROUPED, PATH_DECODE or PATH_SMALL_BATCH for these sizes and flags."""
+    v = int(load_library().moe_path(T, H, I, E, K, flags))
+    if v < 0:
+        _check(v)
+    return v
 
 
 def moe_route(topk_ids, E, m_tile, stream=None) -> dict:

@@ -45,10 +45,22 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   return dot8(u32x4_t{a.x, a.y, a.z, a.w}, u32x4_t{b.x, b.y, b.z, b.w});
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                            false);
+  return v + __builtin_bit_cast(float, m);
+}
+
+// Sum over the wave with DPP moves (no LDS round trips); the total ends up
+// in lane 63.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);       // row_half_mirror
+  v = dpp_add<0x140>(v);       // row_mirror: every lane holds its row's sum
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  return dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
 }
 
 // One wave per (slot, IPW consecutive intermediate columns): the IPW gate
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup(
   for (int r = 0; r < 2 * IPW; ++r) s[r] = wave_sum(s[r]);
 #pragma unroll
   for (int r = 0; r < IPW; ++r) {
-    if (lane == r && i0 + r < I) {
+    if (lane == 63 && i0 + r < I) {
       const float g = s[r], u = s[IPW + r];
       const float a = g / (1.0f + __expf(-g)) * u;
       const __bf16 b = (__bf16)a;  // round to nearest even
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void decode_down(
     s += okj[j] ? d : 0.f;
   }
   s = wave_sum(s);
-  if (lane == 0) out[t * H + h] = s;
+  if (lane == 63) out[t * H + h] = s;
 }
 
 }  // namespace

@@ -36,12 +36,20 @@ int hip_error(const char* what, hipError_t st) {
   return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(st));
 }
 
-// The weight-streaming path reads each routed slot's expert weights on its
-// own; the grouped path reads each routed expert once but has a fixed cost
-// (routing, sparse tiles). Measured crossover: T*K of about E + 16 slots
-// (24 at E=8/top-2, ~144 at E=128/top-8), capped for very many experts.
-constexpr int64_t kDecodeSlotsOverE = 16;
-constexpr int64_t kDecodeMaxSlots = 256;
+// Path choice, from a measured sweep of T = 1..512 on four expert shapes
+// (H/I/E/top-k 2048/768/128/8, 2048/2048/8/2, 4096/384/128/8,
+// 4096/4096/8/2) with uniform routing:
+//  - per-token streaming (two kernels, no combine) is fastest while slots
+//    rarely share an expert: T*K <= max(K, E/2);
+//  - the per-expert small-batch path streams each routed expert once, like
+//    the grouped path, but spends about 1.4e-7 us per T*K*H*I on its vector
+//    dot products; it wins until that reaches the grouped path's extra cost
+//    over streaming the weights (routing, sparse tiles, the fp32 slot
+//    buffer), measured as about 60 us + 0.06 us per MB of routed weights;
+//  - the grouped MFMA path beyond.
+constexpr double kSmallBatchUsPerWork = 1.4e-7;
+constexpr double kGroupedFixedUs = 60.0;
+constexpr double kGroupedUsPerWeightMB = 0.06;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -73,15 +81,29 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   return MOE_OK;
 }
 
+int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  const bool dec = moe::decode_supported(H, I, K);
+  const bool sb = moe::small_batch_supported(T, H, I, K);
+  if ((flags & MOE_FLAG_FORCE_DECODE) && dec) return MOE_PATH_DECODE;
+  if ((flags & MOE_FLAG_FORCE_SMALL_BATCH) && sb) return MOE_PATH_SMALL_BATCH;
+  if (flags & (MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_SMALL_BATCH))
+    return MOE_PATH_GROUPED;
+  const int64_t slots = T * K;
+  if (dec && slots <= std::max<int64_t>(K, E / 2)) return MOE_PATH_DECODE;
+  const double routed_mb = (double)std::min<int64_t>(E, slots) * 6.0 * H * I / 1e6;
+  const double sb_extra_us = kSmallBatchUsPerWork * (double)slots * H * I;
+  if (sb && sb_extra_us <= kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb)
+    return MOE_PATH_SMALL_BATCH;
+  return MOE_PATH_GROUPED;
+}
+
 bool use_decode(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
-  if (!moe::decode_supported(H, I, K)) return false;
-  if (flags & MOE_FLAG_FORCE_DECODE) return true;
-  if (flags & MOE_FLAG_FORCE_GROUPED) return false;
-  return T * K <= std::min<int64_t>(E + kDecodeSlotsOverE, kDecodeMaxSlots);
+  return pick_path(T, H, I, E, K, flags) == MOE_PATH_DECODE;
 }
 
 // Byte offsets of every buffer inside one workspace.
 struct Layout {
+  int path = MOE_PATH_GROUPED;
   bool decode = false;
   moe::GemmCfg g1{}, g2{};
   int64_t cap = 0, max_tiles = 0, nblk = 0;
@@ -99,9 +121,16 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
     return at;
   };
   L.err = take(sizeof(int32_t));
-  if (use_decode(T, H, I, E, K, flags)) {
+  L.path = pick_path(T, H, I, E, K, flags);
+  if (L.path == MOE_PATH_DECODE) {
     L.decode = true;
     L.act = take((size_t)n * I * 2);
+    L.total = p;
+    return L;
+  }
+  if (L.path == MOE_PATH_SMALL_BATCH) {
+    L.act = take((size_t)n * I * 2);
+    L.y = take((size_t)n * H * 4);
     L.total = p;
     return L;
   }
@@ -206,6 +235,12 @@ int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   return use_decode(T, H, I, E, K, flags) ? 1 : 0;
 }
 
+int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  return pick_path(T, H, I, E, K, flags);
+}
+
 int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
                    const int32_t* topk_ids, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
                    float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
@@ -243,6 +278,13 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const flo
     hipError_t st = moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
                                        at<uint16_t>(ws, L.act), out, stream);
     if ((rc = stage_check(flags, "decode", st, stream)) != MOE_OK) return rc;
+  } else if (L.path == MOE_PATH_SMALL_BATCH) {
+    float* y = at<float>(ws, L.y);
+    hipError_t st = moe::launch_small_batch(x, wa, wb, topk_ids, T, H, I, E, K,
+                                            at<uint16_t>(ws, L.act), y, stream);
+    if ((rc = stage_check(flags, "small_batch", st, stream)) != MOE_OK) return rc;
+    st = moe::launch_combine(y, topk_weights, nullptr, topk_ids, E, T, H, K, out, stream);
+    if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
   } else {
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -269,7 +311,7 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const flo
       st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
                              K, L.max_tiles, y, nullptr, stream);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
-      st = moe::launch_combine(y, topk_weights, slot_of, T, H, K, out, stream);
+      st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, out, stream);
       if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
     }
   }

@@ -59,8 +59,11 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
                         hipStream_t stream);
 
+// A slot is dropped if slot_of[f] < 0, or, without slot_of, if its id is
+// outside [0, E).
 hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
-                          int64_t T, int64_t H, int64_t K, float* out, hipStream_t stream);
+                          const int32_t* topk_ids, int64_t E, int64_t T, int64_t H, int64_t K,
+                          float* out, hipStream_t stream);
 hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
 
 // Sets *err_flag to 1 if any id is outside [0, E) or repeats within a token.
@@ -68,6 +71,15 @@ hipError_t launch_validate_ids(const int32_t* ids, int64_t T, int64_t K, int64_t
                                int32_t* err_flag, hipStream_t stream);
 
 bool decode_supported(int64_t H, int64_t I, int64_t K);
+
+// Expert-deduplicated small-batch path (small_batch.hip): act bf16 [T*K, I]
+// and unscaled per-slot outputs y fp32 [T*K, H], then launch_combine.
+constexpr int kSmallBatchMaxSlots = 1024;
+bool small_batch_supported(int64_t T, int64_t H, int64_t I, int64_t K);
+hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
+                              const int32_t* topk_ids, int64_t T, int64_t H, int64_t I,
+                              int64_t E, int64_t K, uint16_t* act, float* y,
+                              hipStream_t stream);
 
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int64_t K,
                                bool renormalize, float* weights, int32_t* ids,

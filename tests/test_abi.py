@@ -30,7 +30,7 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
-              "moe_uses_decode_path", "moe_topk_softmax"):
+              "moe_uses_decode_path", "moe_topk_softmax", "moe_path"):
         assert n in names
 
 
@@ -90,3 +90,25 @@ def test_workspace_and_tile_queries(lib):
     assert not moe.moe_uses_decode_path(1, 2048, 768, 128, 8, moe.FLAG_FORCE_GROUPED)
     with pytest.raises(moe.MoeError):
         moe.moe_m_tile(1, 100, 128, 8, 2)
+
+
+def test_path_choice(lib):
+    assert moe.moe_path(1, 2048, 768, 128, 8) == moe.PATH_DECODE
+    assert moe.moe_path(4195, 2048, 2048, 8, 2) == moe.PATH_GROUPED
+    fl = moe.FLAG_FORCE_SMALL_BATCH
+    assert moe.moe_path(100, 2048, 2048, 8, 2, fl) == moe.PATH_SMALL_BATCH
+    # past the small-batch slot limit the forced path falls back to grouped
+    assert moe.moe_path(600, 2048, 2048, 8, 2, fl) == moe.PATH_GROUPED
+    assert moe.moe_path(1, 2048, 768, 128, 8, moe.FLAG_FORCE_GROUPED) == moe.PATH_GROUPED
+    # default choice by size (the measured crossovers)
+    assert moe.moe_path(8, 2048, 768, 128, 8) == moe.PATH_DECODE
+    assert moe.moe_path(32, 2048, 768, 128, 8) == moe.PATH_SMALL_BATCH
+    assert moe.moe_path(128, 2048, 768, 128, 8) == moe.PATH_GROUPED
+    assert moe.moe_path(2, 2048, 2048, 8, 2) == moe.PATH_DECODE
+    assert moe.moe_path(16, 2048, 2048, 8, 2) == moe.PATH_SMALL_BATCH
+    assert moe.moe_path(135, 2048, 2048, 8, 2) == moe.PATH_GROUPED
+    assert moe.moe_uses_decode_path(8, 2048, 768, 128, 8)
+    assert not moe.moe_uses_decode_path(32, 2048, 768, 128, 8)
+    # the small-batch workspace holds the bf16 activations and fp32 slot rows
+    ws = moe.moe_workspace_bytes(100, 2048, 2048, 8, 2, fl)
+    assert ws >= 200 * 2048 * 2 + 200 * 2048 * 4

@@ -5,8 +5,8 @@ import torch
 
 import moe_topk_ids_amd as moe
 import oracle
-from gpu_helpers import (assert_close, cpu_inputs, oracle_rows, require_gpu, sample_rows, say,
-                         shape_inputs, to_device)
+from gpu_helpers import (assert_close, cpu_inputs, oracle_rows, rel_l2, require_gpu, sample_rows,
+                         say, shape_inputs, to_device)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -15,6 +15,7 @@ PATHS = {
     "slot": moe.FLAG_FORCE_GROUPED,
     "atomic": moe.FLAG_FORCE_GROUPED | moe.FLAG_ATOMIC_COMBINE,
     "decode": moe.FLAG_FORCE_DECODE,
+    "small_batch": moe.FLAG_FORCE_SMALL_BATCH,
 }
 
 
@@ -62,6 +63,52 @@ def test_decode_path_matches_oracle(name):
     rows = sample_rows(got.shape[0], 64, seed=2)
     assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
                  f"decode-path/{name}")
+
+
+# leading tokens per workload for the expert-deduplicated path (T*K <= 1024)
+SB_TOKENS = {"tiny": 64, "prefill": 512, "decode": 1, "wide": 128, "large": 96}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_small_batch_path_matches_oracle(name):
+    """Each routed expert's rows streamed once for all of its slots: every
+    workload's leading tokens, every gate/up and down kernel variant."""
+    require_gpu()
+    s = SHAPES[name]
+    n = SB_TOKENS[name]
+    d = {k: (v[:n] if k in ("hidden_states", "topk_weights", "topk_ids", "router_logits")
+             else v) for k, v in shape_inputs(name).items()}
+    assert moe.moe_path(n, s.H, s.I, s.E, s.K, moe.FLAG_FORCE_SMALL_BATCH) == \
+        moe.PATH_SMALL_BATCH
+    dd = to_device(d)
+    say(f"small-batch path on {name} (T={n})")
+    got = _run(dd, moe.FLAG_FORCE_SMALL_BATCH)
+    rows = sample_rows(n, 64, seed=3)
+    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"small-batch/{name}")
+    # the same slots on the per-token path: equal up to the order of the
+    # fp32 dot products inside each row
+    other = _run(dd, moe.FLAG_FORCE_DECODE)
+    r = rel_l2(got, other)
+    say(f"small-batch vs per-token path: rel-L2 {r:.2e}")
+    assert r <= 2e-3
+
+
+def test_small_batch_repeated_and_shared_experts():
+    """Every token routes to the same two experts (1024 slots on one expert
+    pair), and repeated ids inside a token (a precondition violation whose
+    result is still the weighted sum, linear in the weights)."""
+    require_gpu()
+    d = dict(cpu_inputs(512, 256, 384, 16, 2, seed=11))
+    ids = d["topk_ids"].clone()
+    ids[:, 0] = 5
+    ids[:, 1] = 12
+    ids[7, 1] = 5  # token 7 routes twice to expert 5
+    d["topk_ids"] = ids.contiguous()
+    rows = np.arange(512)
+    got = _run(to_device(d), moe.FLAG_FORCE_SMALL_BATCH)
+    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 "small-batch/shared")
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill", "wide"])
@@ -136,7 +183,7 @@ def test_atomic_path_is_deterministic_for_top2(name):
     (1, 128, 128, 1, 1), (37, 128, 256, 4, 4), (129, 256, 128, 16, 1), (1000, 384, 640, 6, 3),
     (3, 512, 256, 8, 2), (20, 128, 128, 128, 8), (300, 256, 384, 64, 6),
 ])
-@pytest.mark.parametrize("path", ["slot", "atomic", "decode"])
+@pytest.mark.parametrize("path", ["slot", "atomic", "decode", "small_batch"])
 def test_ragged_and_degenerate_shapes(T, H, I, E, K, path):
     require_gpu()
     d = cpu_inputs(T, H, I, E, K, seed=T + E)
@@ -158,7 +205,7 @@ def test_all_tokens_one_expert_and_empty_experts():
     dd = to_device(d)
     rows = np.arange(700)
     want = oracle_rows(d, rows)
-    for path in ("slot", "atomic"):
+    for path in ("slot", "atomic", "small_batch"):
         assert_close(_run(dd, PATHS[path]), want, oracle_rows(d, rows, bf16_inter=True),
                      f"one-expert/{path}")
 
@@ -176,7 +223,7 @@ def test_out_of_range_ids_are_dropped():
     ref = dict(d, topk_weights=zeroed)
     rows = np.arange(64)
     want = oracle_rows(ref, rows)
-    for path in ("slot", "atomic", "decode"):
+    for path in ("slot", "atomic", "decode", "small_batch"):
         got = _run(to_device(bad), PATHS[path])
         assert_close(got, want, None, f"dropped-ids/{path}")
 
@@ -227,6 +274,41 @@ def test_caller_workspace_and_side_stream():
                               dd["topk_ids"], flags=PATHS["slot"], workspace=ws)
     side.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_decode_path_with_caller_workspace_of_garbage():
+    """The small-batch path with a caller workspace full of arbitrary bytes
+    gives the internal-workspace result, twice in a row."""
+    require_gpu()
+    s = SHAPES["decode"]
+    dd = to_device(shape_inputs("decode"))
+    fl = moe.FLAG_FORCE_DECODE
+    ref = _run(dd, fl)
+    nbytes = moe.moe_workspace_bytes(s.T, s.H, s.I, s.E, s.K, fl)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        out = moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                              dd["topk_ids"], flags=fl, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_decode_after_grouped_calls_and_back_to_back():
+    """Grouped calls between small-batch calls share the internal workspace;
+    40 small-batch calls queued without a host sync all give the same bits;
+    so does the debug-sync flag."""
+    require_gpu()
+    dd = to_device(shape_inputs("decode"))
+    tiny = to_device(shape_inputs("tiny"))
+    ref = _run(dd, None)
+    _run(tiny, PATHS["slot"])
+    assert np.array_equal(_run(dd, None), ref)
+    outs = [moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                            dd["topk_ids"]) for _ in range(40)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy(), ref)
+    assert np.array_equal(_run(dd, moe.FLAG_DEBUG_SYNC), ref)
 
 
 def test_debug_sync_flag():
