@@ -111,6 +111,18 @@ def make_inputs(T: int, H: int, I: int, E: int, K: int, seed: int = 0) -> dict:
             "topk_ids": ids, "router_logits": logits}
 
 
+def make_biases(H: int, I: int, E: int, seed: int = 0) -> dict:
+    """Seeded fp32 expert biases (CPU): b1 [E, 2I] (gate biases, then up
+    biases) N(0,1)*0.1, the spread of the gate/up projections under the
+    input recipe above; b2 [E, H] N(0,1)*0.01, about that of one expert's
+    down projection. The pages give no generator for biases."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 1000003)
+    b1 = torch.randn(E, 2 * I, dtype=torch.float32, generator=g) * 0.1
+    b2 = torch.randn(E, H, dtype=torch.float32, generator=g) * 0.01
+    return {"b1": b1.contiguous(), "b2": b2.contiguous()}
+
+
 def make_shape_inputs(name: str, seed: int = 0) -> dict:
     s = SHAPES[name]
     return make_inputs(s.T, s.H, s.I, s.E, s.K, seed=seed)

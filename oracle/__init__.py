@@ -43,6 +43,13 @@ def _load():
     lib.oracle_moe_forward.restype = None
     lib.oracle_moe_forward_f64.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p]
     lib.oracle_moe_forward_f64.restype = None
+    f32, f64 = ctypes.c_float, ctypes.c_double
+    lib.oracle_moe_forward_act.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int,
+                                           f32, f32, p, p, ctypes.c_int, p]
+    lib.oracle_moe_forward_act.restype = None
+    lib.oracle_moe_forward_act_f64.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64,
+                                               ctypes.c_int, f64, f64, p, p, p]
+    lib.oracle_moe_forward_act_f64.restype = None
     lib.oracle_slot_act_bf16.argtypes = [p, p, p, i64, i64, i64, i64, i64, p]
     lib.oracle_slot_act_bf16.restype = None
     lib.oracle_topk_softmax.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p]
@@ -116,6 +123,56 @@ def moe_forward_f64(x, w1, w2, topk_weights, topk_ids) -> np.ndarray:
     out = np.zeros((T, H), np.float64)
     lib.oracle_moe_forward_f64(_ptr(x), _ptr(w1), _ptr(w2), _ptr(tw), _ptr(ids), T, H, I, E, K,
                                _ptr(out))
+    return out
+
+
+ACTIVATIONS = {"silu": 0, "gelu_tanh": 1, "swigluoai": 2, "gelu_erf": 3}
+
+
+def _opt(a, dtype):
+    return None if a is None else _c(a, dtype)
+
+
+def _optptr(a):
+    return None if a is None else _ptr(a)
+
+
+def moe_forward_act(x, w1, w2, topk_weights, topk_ids, act: str = "silu", alpha: float = 1.702,
+                    limit: float = 7.0, b1=None, b2=None, bf16_inter: bool = False) -> np.ndarray:
+    """fp32 oracle forward with an activation variant and optional fp32
+    biases b1 [E, 2I] (gate, then up) and b2 [E, H]."""
+    lib = _load()
+    x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
+    tw, ids = _c(topk_weights, np.float32), _c(topk_ids, np.int32)
+    b1, b2 = _opt(b1, np.float32), _opt(b2, np.float32)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    K = ids.shape[1]
+    assert b1 is None or b1.shape == (E, 2 * I)
+    assert b2 is None or b2.shape == (E, H)
+    out = np.zeros((T, H), np.float32)
+    lib.oracle_moe_forward_act(_ptr(x), _ptr(w1), _ptr(w2), _ptr(tw), _ptr(ids), T, H, I, E, K,
+                               ACTIVATIONS[act], alpha, limit, _optptr(b1), _optptr(b2),
+                               1 if bf16_inter else 0, _ptr(out))
+    return out
+
+
+def moe_forward_act_f64(x, w1, w2, topk_weights, topk_ids, act: str = "silu",
+                        alpha: float = 1.702, limit: float = 7.0, b1=None, b2=None) -> np.ndarray:
+    """The same definition in fp64 (weights and biases widened)."""
+    lib = _load()
+    x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
+    tw, ids = _c(topk_weights, np.float64), _c(topk_ids, np.int32)
+    b1, b2 = _opt(b1, np.float64), _opt(b2, np.float64)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    K = ids.shape[1]
+    out = np.zeros((T, H), np.float64)
+    lib.oracle_moe_forward_act_f64(_ptr(x), _ptr(w1), _ptr(w2), _ptr(tw), _ptr(ids), T, H, I, E,
+                                   K, ACTIVATIONS[act], alpha, limit, _optptr(b1), _optptr(b2),
+                                   _ptr(out))
     return out
 
 

@@ -18,6 +18,15 @@
  *   [tpu-ref]    tpu-inference fused_moe v1 kernel.py, function ref_moe: the
  *                same computation walked per token, per chosen expert, with
  *                the per-token outputs summed with the top-k weights.
+ *   [tpu-v2]     tpu-inference fused_moe kernel.py, the later version:
+ *                activation_fn (silu(g)*u, gelu(g)*u with jax.nn.gelu's
+ *                default tanh form, swigluoai), swigluoai (gate clipped from
+ *                above and up clipped to [-limit, limit], then
+ *                (up + 1) * gate * sigmoid(alpha * gate), alpha 1.702 and
+ *                limit 7 by default), and ref_moe's optional fp32 biases: b1
+ *                added to the gate and up projections before the
+ *                activation, b2 added to each expert's down projection
+ *                before the routing weight.
  *   [tpu-scatter] tpu-inference fused_moe v1 kernel.py, start_a2a_scatter:
  *                (token, k) pairs are placed into per-expert contiguous
  *                buffers by walking tokens in order and, inside a token, the
@@ -128,15 +137,55 @@ int oracle_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int64_t M,
 }
 
 /* ------------------------------------------------------------------ */
+/* Gated activations ([atrex-009] silu; [tpu-v2] activation_fn)        */
+/* ------------------------------------------------------------------ */
+
+enum { ORA_ACT_SILU = 0, ORA_ACT_GELU_TANH = 1, ORA_ACT_SWIGLUOAI = 2, ORA_ACT_GELU_ERF = 3 };
+
+/* act(g, u) in fp32, each operation rounded separately. */
+static float ora_act_f32(float g, float u, int act, float alpha, float limit) {
+  if (act == ORA_ACT_GELU_TANH) {
+    /* 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) */
+    const float inner = 0.7978845608028654f * (g + 0.044715f * (g * g * g));
+    return (0.5f * g * (1.0f + tanhf(inner))) * u;
+  }
+  if (act == ORA_ACT_GELU_ERF) /* 0.5 g (1 + erf(g / sqrt 2)) */
+    return (0.5f * g * (1.0f + erff(g * 0.7071067811865476f))) * u;
+  if (act == ORA_ACT_SWIGLUOAI) {
+    const float gc = g < limit ? g : limit;
+    const float uc = u < -limit ? -limit : (u > limit ? limit : u);
+    const float glu = gc / (1.0f + expf(-(alpha * gc)));
+    return (uc + 1.0f) * glu;
+  }
+  return (g / (1.0f + expf(-g))) * u; /* silu(g) * u */
+}
+
+static double ora_act_f64(double g, double u, int act, double alpha, double limit) {
+  if (act == ORA_ACT_GELU_TANH) {
+    const double inner = 0.79788456080286535588 * (g + 0.044715 * g * g * g);
+    return 0.5 * g * (1.0 + tanh(inner)) * u;
+  }
+  if (act == ORA_ACT_GELU_ERF) return 0.5 * g * (1.0 + erf(g * 0.70710678118654752440)) * u;
+  if (act == ORA_ACT_SWIGLUOAI) {
+    const double gc = g < limit ? g : limit;
+    const double uc = u < -limit ? -limit : (u > limit ? limit : u);
+    return (uc + 1.0) * (gc / (1.0 + exp(-alpha * gc)));
+  }
+  return g / (1.0 + exp(-g)) * u;
+}
+
+/* ------------------------------------------------------------------ */
 /* One expert applied to one token, fp32 ([atrex-009] Model.forward)   */
 /* ------------------------------------------------------------------ */
 
 /*
- * act[i] = silu(g[i]) * u[i] with g[i] = sum_h x[h]*w1[e,i,h] and
- * u[i] = sum_h x[h]*w1[e,I+i,h], fp32, h ascending. If bf16_inter, act is
- * rounded to bf16 (RNE) and returned widened back to fp32.
+ * act[i] = act(g[i], u[i]) with g[i] = sum_h x[h]*w1[e,i,h] (+ b1e[i]) and
+ * u[i] = sum_h x[h]*w1[e,I+i,h] (+ b1e[I+i]), fp32, h ascending; b1e may be
+ * NULL (no bias). If bf16_inter, act is rounded to bf16 (RNE) and returned
+ * widened back to fp32.
  */
 static void ora_expert_act_f32(const uint16_t* x, const uint16_t* w1e, int64_t H, int64_t I,
+                               int act_kind, float alpha, float limit, const float* b1e,
                                int bf16_inter, float* act) {
   for (int64_t i = 0; i < I; ++i) {
     const uint16_t* wg = w1e + i * H;
@@ -147,8 +196,11 @@ static void ora_expert_act_f32(const uint16_t* x, const uint16_t* w1e, int64_t H
       g = g + xv * ora_bf16_to_f32(wg[h]);
       u = u + xv * ora_bf16_to_f32(wu[h]);
     }
-    float s = g / (1.0f + expf(-g));
-    float a = s * u;
+    if (b1e) {
+      g = g + b1e[i];
+      u = u + b1e[I + i];
+    }
+    float a = ora_act_f32(g, u, act_kind, alpha, limit);
     if (bf16_inter) a = ora_bf16_to_f32(ora_f32_to_bf16_rne(a));
     act[i] = a;
   }
@@ -172,10 +224,18 @@ static void ora_expert_down_f32(const float* act, const uint16_t* w2e, int64_t H
  * Slots whose id lies outside [0, E) contribute nothing.
  * x: bf16 [T,H]; w1: bf16 [E,2I,H]; w2: bf16 [E,H,I]; out: fp32 [T,H].
  */
-void oracle_moe_forward(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
-                        const float* topk_weights, const int32_t* topk_ids, int64_t T,
-                        int64_t H, int64_t I, int64_t E, int64_t K, int bf16_inter,
-                        float* out) {
+/*
+ * With an activation variant and optional biases ([tpu-v2] ref_moe):
+ * act_kind 0 silu, 1 gelu (tanh form), 2 swigluoai(alpha, limit), 3 gelu
+ * (erf form); b1 fp32 [E, 2I] (gate biases, then up biases) or NULL; b2 fp32
+ * [E, H] or NULL, added to y before the routing weight:
+ *   out[t,h] = sum_k topk_weights[t,k] * (y_{t,k}[h] + b2[e,h]).
+ */
+void oracle_moe_forward_act(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                            const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                            int64_t H, int64_t I, int64_t E, int64_t K, int act_kind,
+                            float alpha, float limit, const float* b1, const float* b2,
+                            int bf16_inter, float* out) {
 #pragma omp parallel
   {
     float* act = (float*)malloc((size_t)I * sizeof(float));
@@ -188,14 +248,25 @@ void oracle_moe_forward(const uint16_t* x, const uint16_t* w1, const uint16_t* w
         int32_t e = topk_ids[t * K + k];
         if (e < 0 || e >= E) continue;
         float w = topk_weights[t * K + k];
-        ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, bf16_inter, act);
+        ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, act_kind, alpha, limit,
+                           b1 ? b1 + (int64_t)e * 2 * I : NULL, bf16_inter, act);
         ora_expert_down_f32(act, w2 + (int64_t)e * H * I, H, I, y);
+        if (b2)
+          for (int64_t h = 0; h < H; ++h) y[h] = y[h] + b2[(int64_t)e * H + h];
         for (int64_t h = 0; h < H; ++h) o[h] = o[h] + w * y[h];
       }
     }
     free(act);
     free(y);
   }
+}
+
+void oracle_moe_forward(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                        const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                        int64_t H, int64_t I, int64_t E, int64_t K, int bf16_inter,
+                        float* out) {
+  oracle_moe_forward_act(x, w1, w2, topk_weights, topk_ids, T, H, I, E, K, ORA_ACT_SILU, 0.0f,
+                         0.0f, NULL, NULL, bf16_inter, out);
 }
 
 /*
@@ -218,7 +289,8 @@ void oracle_slot_act_bf16(const uint16_t* x, const uint16_t* w1, const int32_t* 
         for (int64_t i = 0; i < I; ++i) dst[i] = 0;
         continue;
       }
-      ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, 0, act);
+      ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, ORA_ACT_SILU, 0.0f, 0.0f,
+                         NULL, 0, act);
       for (int64_t i = 0; i < I; ++i) dst[i] = ora_f32_to_bf16_rne(act[i]);
     }
     free(act);
@@ -229,9 +301,11 @@ void oracle_slot_act_bf16(const uint16_t* x, const uint16_t* w1, const int32_t* 
 /* fp64 version of the same definition, for pinning the fp32 oracle    */
 /* ------------------------------------------------------------------ */
 
-void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
-                            const double* topk_weights, const int32_t* topk_ids, int64_t T,
-                            int64_t H, int64_t I, int64_t E, int64_t K, double* out) {
+void oracle_moe_forward_act_f64(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                                const double* topk_weights, const int32_t* topk_ids, int64_t T,
+                                int64_t H, int64_t I, int64_t E, int64_t K, int act_kind,
+                                double alpha, double limit, const double* b1, const double* b2,
+                                double* out) {
 #pragma omp parallel
   {
     double* act = (double*)malloc((size_t)I * sizeof(double));
@@ -252,17 +326,29 @@ void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_
             g += xv * (double)ora_bf16_to_f32(w1e[i * H + h]);
             u += xv * (double)ora_bf16_to_f32(w1e[(I + i) * H + h]);
           }
-          act[i] = g / (1.0 + exp(-g)) * u;
+          if (b1) {
+            g += b1[(int64_t)e * 2 * I + i];
+            u += b1[(int64_t)e * 2 * I + I + i];
+          }
+          act[i] = ora_act_f64(g, u, act_kind, alpha, limit);
         }
         for (int64_t h = 0; h < H; ++h) {
           double acc = 0.0;
           for (int64_t i = 0; i < I; ++i) acc += act[i] * (double)ora_bf16_to_f32(w2e[h * I + i]);
+          if (b2) acc += b2[(int64_t)e * H + h];
           o[h] += w * acc;
         }
       }
     }
     free(act);
   }
+}
+
+void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                            const double* topk_weights, const int32_t* topk_ids, int64_t T,
+                            int64_t H, int64_t I, int64_t E, int64_t K, double* out) {
+  oracle_moe_forward_act_f64(x, w1, w2, topk_weights, topk_ids, T, H, I, E, K, ORA_ACT_SILU, 0.0,
+                             0.0, NULL, NULL, out);
 }
 
 /* ------------------------------------------------------------------ */
