@@ -111,6 +111,33 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2,
                    float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Gated activations (the later tpu-inference fused_moe kernel.py,
+ * activation_fn and swigluoai): */
+#define MOE_ACT_SILU 0      /* silu(g) * u                                    */
+#define MOE_ACT_GELU_TANH 1 /* gelu(g) * u, tanh form (jax.nn.gelu's default) */
+#define MOE_ACT_SWIGLUOAI 2 /* (clip(u, -limit, limit) + 1) * gc * sigmoid(alpha * gc),
+                               gc = min(g, limit); alpha 1.702, limit 7 there */
+#define MOE_ACT_GELU_ERF 3  /* gelu(g) * u, erf form                          */
+
+/*
+ * As moe_forward_ex, with a gated activation variant and optional fp32 expert
+ * biases (ref_moe of the later tpu-inference fused_moe kernel.py):
+ *   b1  fp32 [E, 2I] or NULL: b1[e, 0:I] is added to the gate projection and
+ *       b1[e, I:2I] to the up projection, before the activation;
+ *   b2  fp32 [E, H] or NULL: added to expert e's down projection before its
+ *       routing weight: out[t] = sum_k w[t,k] * (y_{t,k} + b2[e_k]).
+ * `alpha` and `limit` are read for MOE_ACT_SWIGLUOAI only (limit >= 0).
+ * Returns MOE_ERR_INVALID_ARG for an unknown activation. moe_forward_ex is
+ * this call with MOE_ACT_SILU and no biases.
+ */
+int moe_forward_act(const void* hidden, const void* w1, const void* w2,
+                    const float* topk_weights, const int32_t* topk_ids,
+                    int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                    int32_t activation, float alpha, float limit,
+                    const float* b1, const float* b2,
+                    float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Bytes of workspace moe_forward_ex needs for these sizes and flags
  * (0 for T == 0). Returns 0 and sets the last error on invalid sizes. */
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,

@@ -26,6 +26,13 @@ FLAG_DEBUG_SYNC = 8
 FLAG_VALIDATE_IDS = 16
 FLAG_FORCE_SMALL_BATCH = 32
 
+ACT_SILU = 0
+ACT_GELU_TANH = 1
+ACT_SWIGLUOAI = 2
+ACT_GELU_ERF = 3
+ACTIVATIONS = {"silu": ACT_SILU, "gelu_tanh": ACT_GELU_TANH, "swigluoai": ACT_SWIGLUOAI,
+               "gelu_erf": ACT_GELU_ERF}
+
 PATH_GROUPED = 0
 PATH_DECODE = 1
 PATH_SMALL_BATCH = 2
@@ -58,6 +65,10 @@ def load_library():
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward_ex.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, u32, p, sz, p]
     lib.moe_forward_ex.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.moe_forward_act.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, f32, f32, p, p,
+                                    p, u32, p, sz, p]
+    lib.moe_forward_act.restype = ctypes.c_int
     lib.moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, u32]
     lib.moe_workspace_bytes.restype = sz
     lib.moe_m_tile.argtypes = [i64, i64, i64, i64, i64, u32]
@@ -114,12 +125,15 @@ def _need(t, name, dtype, ndim):
 
 
 def moe_forward(hidden_states, w1, w2, topk_weights, topk_ids, out=None, flags=None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, activation="silu", alpha=1.702, limit=7.0,
+                b1=None, b2=None):
     """out[T,H] fp32 = sum_k topk_weights[:,k] * expert_{topk_ids[:,k]}(hidden_states).
 
     ``flags=None`` calls ``moe_forward`` (internal workspace, MOE_COMBINE from
     the environment); otherwise ``moe_forward_ex`` with these flags and the
-    optional ``workspace`` (a uint8 device tensor).
+    optional ``workspace`` (a uint8 device tensor). An activation other than
+    "silu" ("gelu_tanh", "gelu_erf", "swigluoai" with ``alpha``/``limit``) or
+    expert biases (fp32 ``b1`` [E, 2I], ``b2`` [E, H]) call ``moe_forward_act``.
     """
     import torch
 
@@ -146,6 +160,26 @@ def moe_forward(hidden_states, w1, w2, topk_weights, topk_ids, out=None, flags=N
             raise ValueError("out must be [T, H]")
     args = (_ptr(hidden_states), _ptr(w1), _ptr(w2), _ptr(topk_weights), _ptr(topk_ids),
             T, H, I, E, K, _ptr(out))
+    if activation != "silu" or b1 is not None or b2 is not None:
+        if activation not in ACTIVATIONS:
+            raise ValueError(f"unknown activation {activation!r}")
+        if b1 is not None:
+            _need(b1, "b1", torch.float32, 2)
+            if tuple(b1.shape) != (E, 2 * I):
+                raise ValueError("b1 must be [E, 2I]")
+        if b2 is not None:
+            _need(b2, "b2", torch.float32, 2)
+            if tuple(b2.shape) != (E, H):
+                raise ValueError("b2 must be [E, H]")
+        ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+        if workspace is not None:
+            _need(workspace, "workspace", torch.uint8, 1)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+        _check(lib.moe_forward_act(
+            *args[:10], ACTIVATIONS[activation], ctypes.c_float(alpha), ctypes.c_float(limit),
+            None if b1 is None else _ptr(b1), None if b2 is None else _ptr(b2), args[10],
+            ctypes.c_uint32(flags or 0), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream)))
+        return out
     if flags is None and workspace is None:
         _check(lib.moe_forward(*args, _stream(stream)))
     else:

@@ -70,7 +70,7 @@ template <int NC, int IPW>
 __global__ __launch_bounds__(kThreads) void decode_gateup(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ topk_ids, int64_t H, int64_t I, int32_t E, int32_t K,
-    uint16_t* __restrict__ act) {
+    uint16_t* __restrict__ act, Epilogue ep) {
   const int lane = threadIdx.x & 63;
   const int64_t i0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * IPW;
   const int64_t f = blockIdx.y;
@@ -114,8 +114,13 @@ __global__ __launch_bounds__(kThreads) void decode_gateup(
 #pragma unroll
   for (int r = 0; r < IPW; ++r) {
     if (lane == 63 && i0 + r < I) {
-      const float g = s[r], u = s[IPW + r];
-      const float a = g / (1.0f + __expf(-g)) * u;
+      float g = s[r], u = s[IPW + r];
+      if (ep.b1) {
+        g += ep.b1[(int64_t)e * 2 * I + i0 + r];
+        u += ep.b1[(int64_t)e * 2 * I + I + i0 + r];
+      }
+      const float a = ep.act == kActSilu ? g / (1.0f + __expf(-g)) * u
+                                         : gated_act(g, u, ep.act, ep.alpha, ep.limit);
       const __bf16 b = (__bf16)a;  // round to nearest even
       act[f * I + i0 + r] = __builtin_bit_cast(uint16_t, b);
     }
@@ -128,7 +133,7 @@ template <int J>
 __global__ __launch_bounds__(kThreads) void decode_down(
     const uint16_t* __restrict__ w2, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ topk_ids, const uint16_t* __restrict__ act, int64_t H,
-    int64_t I, int32_t E, int32_t K, float* __restrict__ out) {
+    int64_t I, int32_t E, int32_t K, const float* __restrict__ b2, float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t h = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t t = blockIdx.y;
@@ -164,10 +169,21 @@ __global__ __launch_bounds__(kThreads) void decode_down(
     av[j] = av_base[okj[j] ? qj[j] : 0];
   }
   float s = 0.f;
+  if (b2) {
+    // expert bias before the routing weight: w_k * (partial + b2[e_k, h]),
+    // added by the lane holding the first chunk of row k
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const float d = wk[j] * dot8(wv[j], av[j]);
-    s += okj[j] ? d : 0.f;
+    for (int j = 0; j < J; ++j) {
+      const float bj = (okj[j] && cj[j] == 0) ? b2[(int64_t)ej[j] * H + h] : 0.f;
+      const float d = wk[j] * (dot8(wv[j], av[j]) + bj);
+      s += okj[j] ? d : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float d = wk[j] * dot8(wv[j], av[j]);
+      s += okj[j] ? d : 0.f;
+    }
   }
   s = wave_sum(s);
   if (lane == 63) out[t * H + h] = s;
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void decode_down(
 hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                          const float* topk_weights, const int32_t* topk_ids, int64_t T,
                          int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,
-                         float* out, hipStream_t stream) {
+                         float* out, const Epilogue& ep, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int64_t nc = (H / 8 + 63) / 64;           // chunks per lane per gate/up row
   const int64_t iters = (K * (I / 8) + 63) / 64;  // chunks per lane in the down kernel
@@ -186,7 +202,8 @@ hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint1
   constexpr int kIPW = 1;  // one gate/up column pair per wave measured fastest
   dim3 g1((unsigned)((I + kIPW * kWaves - 1) / (kIPW * kWaves)), (unsigned)(T * K));
 #define MOE_GATEUP(NN) \
-  decode_gateup<NN, kIPW><<<g1, kThreads, 0, stream>>>(hidden, w1, topk_ids, H, I, (int32_t)E, (int32_t)K, act)
+  decode_gateup<NN, kIPW><<<g1, kThreads, 0, stream>>>(hidden, w1, topk_ids, H, I, (int32_t)E, \
+                                                       (int32_t)K, act, ep)
   if (nc <= 1) MOE_GATEUP(1);
   else if (nc <= 2) MOE_GATEUP(2);
   else if (nc <= 4) MOE_GATEUP(4);
@@ -198,7 +215,7 @@ hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint1
   dim3 g2((unsigned)((H + kWaves - 1) / kWaves), (unsigned)T);
 #define MOE_DOWN(JJ)                                                                     \
   decode_down<JJ><<<g2, kThreads, 0, stream>>>(w2, topk_weights, topk_ids, act, H, I, \
-                                               (int32_t)E, (int32_t)K, out)
+                                               (int32_t)E, (int32_t)K, ep.b2, out)
   if (iters <= 4) MOE_DOWN(4);
   else if (iters <= 8) MOE_DOWN(8);
   else if (iters <= 12) MOE_DOWN(12);

@@ -65,6 +65,11 @@ struct GemmArgs {
   int32_t max_tiles;        // row tiles the grid was sized for
   int32_t n_tiles;          // weight-row tiles
   int32_t group_m;          // row tiles per scheduling group
+  // epilogue variants: activation kind and swigluoai parameters (GEMM1),
+  // bias b1 [E, 2I] (GEMM1) or b2 [E, H] (GEMM2 with the atomic combine)
+  int32_t act;
+  float alpha, limit;
+  const float* bias;
 };
 
 // XOR permutation of the 16-byte chunks of a staged row (CPR chunks per
@@ -390,20 +395,51 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   if (MODE == kGateUpSilu) {
     uint16_t* act = reinterpret_cast<uint16_t*>(args.out);
     const int64_t n0g = (int64_t)ntile * (BN / 2);
+    if (args.act == kActSilu && args.bias == nullptr) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
+      for (int tm = 0; tm < TM; ++tm) {
+        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
 #pragma unroll
-      for (int tn = 0; tn < TN / 2; ++tn) {
-        const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
+        for (int tn = 0; tn < TN / 2; ++tn) {
+          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x16_t& g = acc[tn][tm];
-          const f32x16_t& u = acc[tn + TN / 2][tm];
-          uint2 v;
-          v.x = pack_bf16x2(silu_mul(g[4 * j + 0], u[4 * j + 0]), silu_mul(g[4 * j + 1], u[4 * j + 1]));
-          v.y = pack_bf16x2(silu_mul(g[4 * j + 2], u[4 * j + 2]), silu_mul(g[4 * j + 3], u[4 * j + 3]));
-          *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t& g = acc[tn][tm];
+            const f32x16_t& u = acc[tn + TN / 2][tm];
+            uint2 v;
+            v.x = pack_bf16x2(silu_mul(g[4 * j + 0], u[4 * j + 0]), silu_mul(g[4 * j + 1], u[4 * j + 1]));
+            v.y = pack_bf16x2(silu_mul(g[4 * j + 2], u[4 * j + 2]), silu_mul(g[4 * j + 3], u[4 * j + 3]));
+            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+          }
+        }
+      }
+    } else {  // activation variant and/or gate/up bias
+      const float* b1 = args.bias ? args.bias + (int64_t)e * 2 * args.inter : nullptr;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
+#pragma unroll
+        for (int tn = 0; tn < TN / 2; ++tn) {
+          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t& g = acc[tn][tm];
+            const f32x16_t& u = acc[tn + TN / 2][tm];
+            float a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float gv = g[4 * j + q], uv = u[4 * j + q];
+              if (b1) {
+                gv += b1[col + 8 * j + q];
+                uv += b1[args.inter + col + 8 * j + q];
+              }
+              a[q] = gated_act(gv, uv, args.act, args.alpha, args.limit);
+            }
+            uint2 v;
+            v.x = pack_bf16x2(a[0], a[1]);
+            v.y = pack_bf16x2(a[2], a[3]);
+            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+          }
         }
       }
     }
@@ -432,9 +468,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
           const f32x16_t& a = acc[tn][tm];
           if (MODE == kDownSlot) {
             *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
-          } else {
+          } else if (args.bias == nullptr) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * a[4 * j + i]);
+          } else {  // w * (y + b2[e]), the weight applied to the biased output
+            const float* b2 = args.bias + (int64_t)e * args.n_out + col + 8 * j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * (a[4 * j + i] + b2[i]));
           }
         }
       }
@@ -489,8 +529,13 @@ GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm)
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
-                             int64_t K, int64_t max_tiles, uint16_t* act, hipStream_t stream) {
+                             int64_t K, int64_t max_tiles, uint16_t* act, const Epilogue& ep,
+                             hipStream_t stream) {
   GemmArgs a{};
+  a.act = ep.act;
+  a.alpha = ep.alpha;
+  a.limit = ep.limit;
+  a.bias = ep.b1;
   a.a = hidden;
   a.w = w1;
   a.sorted = sorted;
@@ -512,8 +557,9 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
-                        hipStream_t stream) {
+                        const float* b2, hipStream_t stream) {
   GemmArgs a{};
+  a.bias = out ? b2 : nullptr;  // on the slot path the combine adds b2
   a.a = act;
   a.w = w2;
   a.sorted = sorted;

@@ -241,12 +241,23 @@ int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fla
   return pick_path(T, H, I, E, K, flags);
 }
 
-int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
-                   const int32_t* topk_ids, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
-                   float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
-                   void* stream_ptr) {
+int moe_forward_act(const void* hidden, const void* w1, const void* w2,
+                    const float* topk_weights, const int32_t* topk_ids, int64_t T, int64_t H,
+                    int64_t I, int64_t E, int64_t K, int32_t activation, float alpha,
+                    float limit, const float* b1, const float* b2, float* out, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream_ptr) {
   int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
+  if (activation < MOE_ACT_SILU || activation > MOE_ACT_GELU_ERF)
+    return set_error(MOE_ERR_INVALID_ARG, "unknown activation %d", activation);
+  if (activation == MOE_ACT_SWIGLUOAI && !(limit >= 0.0f && alpha == alpha))
+    return set_error(MOE_ERR_INVALID_ARG, "swigluoai needs limit >= 0 and a numeric alpha");
+  moe::Epilogue ep;
+  ep.act = activation;
+  ep.alpha = alpha;
+  ep.limit = limit;
+  ep.b1 = b1;
+  ep.b2 = b2;
   if (T == 0) return MOE_OK;
   if (!hidden || !w1 || !w2 || !topk_weights || !topk_ids || !out)
     return set_error(MOE_ERR_INVALID_ARG, "null device pointer with T=%lld", (long long)T);
@@ -276,14 +287,14 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const flo
 
   if (L.decode) {
     hipError_t st = moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
-                                       at<uint16_t>(ws, L.act), out, stream);
+                                       at<uint16_t>(ws, L.act), out, ep, stream);
     if ((rc = stage_check(flags, "decode", st, stream)) != MOE_OK) return rc;
   } else if (L.path == MOE_PATH_SMALL_BATCH) {
     float* y = at<float>(ws, L.y);
     hipError_t st = moe::launch_small_batch(x, wa, wb, topk_ids, T, H, I, E, K,
-                                            at<uint16_t>(ws, L.act), y, stream);
+                                            at<uint16_t>(ws, L.act), y, ep, stream);
     if ((rc = stage_check(flags, "small_batch", st, stream)) != MOE_OK) return rc;
-    st = moe::launch_combine(y, topk_weights, nullptr, topk_ids, E, T, H, K, out, stream);
+    st = moe::launch_combine(y, topk_weights, nullptr, topk_ids, E, T, H, K, ep.b2, out, stream);
     if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
   } else {
     int32_t* counts = at<int32_t>(ws, L.counts);
@@ -298,20 +309,21 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const flo
                                       sorted, slot_of, tile_expert, num_tiles, stream);
     if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
     st = moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I, K,
-                                L.max_tiles, act, stream);
+                                L.max_tiles, act, ep, stream);
     if ((rc = stage_check(flags, "gemm1_silu", st, stream)) != MOE_OK) return rc;
     if (flags & MOE_FLAG_ATOMIC_COMBINE) {
       st = moe::launch_zero(out, T * H, stream);
       if ((rc = stage_check(flags, "zero_out", st, stream)) != MOE_OK) return rc;
       st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
-                             K, L.max_tiles, nullptr, out, stream);
+                             K, L.max_tiles, nullptr, out, ep.b2, stream);
       if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
     } else {
       float* y = at<float>(ws, L.y);
       st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
-                             K, L.max_tiles, y, nullptr, stream);
+                             K, L.max_tiles, y, nullptr, nullptr, stream);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
-      st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, out, stream);
+      st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2, out,
+                               stream);
       if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
     }
   }
@@ -327,6 +339,15 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const flo
                        (long long)E);
   }
   return MOE_OK;
+}
+
+int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
+                   const int32_t* topk_ids, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                   float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return moe_forward_act(hidden, w1, w2, topk_weights, topk_ids, T, H, I, E, K, MOE_ACT_SILU,
+                         1.702f, 7.0f, nullptr, nullptr, out, flags, workspace, workspace_bytes,
+                         stream);
 }
 
 int moe_forward(const void* hidden, const void* w1, const void* w2, const float* topk_weights,
@@ -392,7 +413,7 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
   hipError_t st = moe::launch_gemm1_silu(
       moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256}, static_cast<const uint16_t*>(hidden),
       static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
-      static_cast<uint16_t*>(act), static_cast<hipStream_t>(stream));
+      static_cast<uint16_t*>(act), moe::Epilogue{}, static_cast<hipStream_t>(stream));
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
 }
 

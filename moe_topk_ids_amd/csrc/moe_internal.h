@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "activation.h"
+
 namespace moe {
 
 // Slots handled by one routing workgroup (grows with T*K so that the number
@@ -48,22 +50,24 @@ GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm)
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
-                             int64_t K, int64_t max_tiles, uint16_t* act, hipStream_t stream);
+                             int64_t K, int64_t max_tiles, uint16_t* act, const Epilogue& ep,
+                             hipStream_t stream);
 
-// Down projection. If `out` is non-null the tile results are scaled by the
-// routing weight and atomically added to out[t, :]; otherwise they are
-// written unscaled to y[f, :] (f = t*K + k).
+// Down projection. If `out` is non-null the tile results (plus b2[e], if
+// given) are scaled by the routing weight and atomically added to out[t, :];
+// otherwise they are written unscaled and unbiased to y[f, :] (f = t*K + k).
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
-                        hipStream_t stream);
+                        const float* b2, hipStream_t stream);
 
+// out[t, :] = sum_k w[t,k] * (y[t*K+k, :] + b2[e_k, :]) (b2 may be null).
 // A slot is dropped if slot_of[f] < 0, or, without slot_of, if its id is
 // outside [0, E).
 hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
                           const int32_t* topk_ids, int64_t E, int64_t T, int64_t H, int64_t K,
-                          float* out, hipStream_t stream);
+                          const float* b2, float* out, hipStream_t stream);
 hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
 
 // Sets *err_flag to 1 if any id is outside [0, E) or repeats within a token.
@@ -79,7 +83,7 @@ bool small_batch_supported(int64_t T, int64_t H, int64_t I, int64_t K);
 hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                               const int32_t* topk_ids, int64_t T, int64_t H, int64_t I,
                               int64_t E, int64_t K, uint16_t* act, float* y,
-                              hipStream_t stream);
+                              const Epilogue& ep, hipStream_t stream);
 
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int64_t K,
                                bool renormalize, float* weights, int32_t* ids,
@@ -88,6 +92,6 @@ hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int64_
 hipError_t launch_decode(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                          const float* topk_weights, const int32_t* topk_ids, int64_t T,
                          int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,
-                         float* out, hipStream_t stream);
+                         float* out, const Epilogue& ep, hipStream_t stream);
 
 }  // namespace moe

@@ -115,6 +115,7 @@ struct SbArgs {
   float* y;       // fp32 [n, H]
   int64_t H, I;
   int32_t E, K, n;
+  Epilogue ep;  // activation variant and gate/up bias (b2 is the combine's)
 };
 
 // NC: 16-byte chunks per lane per gate/up row (H / 512 rounded up).
@@ -179,7 +180,13 @@ __global__ __launch_bounds__(kThreads) void sb_gateup(SbArgs a) {
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
       if (lane == 63 && m0 + b < count) {
-        const float v = g[b] / (1.0f + __expf(-g[b])) * u[b];
+        if (a.ep.b1) {
+          g[b] += a.ep.b1[(int64_t)e * 2 * I + i];
+          u[b] += a.ep.b1[(int64_t)e * 2 * I + I + i];
+        }
+        const float v = a.ep.act == kActSilu
+                            ? g[b] / (1.0f + __expf(-g[b])) * u[b]
+                            : gated_act(g[b], u[b], a.ep.act, a.ep.alpha, a.ep.limit);
         const __bf16 bv = (__bf16)v;  // round to nearest even
         a.act[(int64_t)s_slots[m0 + b] * I + i] = __builtin_bit_cast(uint16_t, bv);
       }
@@ -266,7 +273,7 @@ bool small_batch_supported(int64_t T, int64_t H, int64_t I, int64_t K) {
 hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const uint16_t* w2,
                               const int32_t* topk_ids, int64_t T, int64_t H, int64_t I,
                               int64_t E, int64_t K, uint16_t* act, float* y,
-                              hipStream_t stream) {
+                              const Epilogue& ep, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (!small_batch_supported(T, H, I, K)) return hipErrorInvalidValue;
   SbArgs a;
@@ -281,6 +288,7 @@ hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const 
   a.E = (int32_t)E;
   a.K = (int32_t)K;
   a.n = (int32_t)(T * K);
+  a.ep = ep;
   // one workgroup row per possibly-present expert; absent ranks exit
   const unsigned gy = (unsigned)(a.n < E ? a.n : E);
   const int64_t nc = (H / 8 + 63) / 64;

@@ -30,7 +30,7 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
-              "moe_uses_decode_path", "moe_topk_softmax", "moe_path"):
+              "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act"):
         assert n in names
 
 
@@ -59,6 +59,21 @@ def test_size_validation_without_device(lib):
     assert rc == moe.MOE_ERR_INVALID_ARG
     # T == 0 is a no-op success even with null pointers
     assert lib.moe_forward(p, p, p, p, p, 0, 128, 128, 8, 2, p, p) == moe.MOE_OK
+
+
+def test_activation_argument_validation(lib):
+    p = ctypes.c_void_p(0)
+    f = ctypes.c_float
+    # unknown activation; swigluoai with a negative limit
+    assert lib.moe_forward_act(p, p, p, p, p, 4, 128, 128, 8, 2, 7, f(1.0), f(7.0), p, p, p, 0, p,
+                               0, p) == moe.MOE_ERR_INVALID_ARG
+    assert b"activation" in lib.moe_last_error()
+    assert lib.moe_forward_act(p, p, p, p, p, 4, 128, 128, 8, 2, moe.ACT_SWIGLUOAI, f(1.0),
+                               f(-1.0), p, p, p, 0, p, 0, p) == moe.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op for every activation
+    for a in range(4):
+        assert lib.moe_forward_act(p, p, p, p, p, 0, 128, 128, 8, 2, a, f(1.702), f(7.0), p, p, p,
+                                   0, p, 0, p) == moe.MOE_OK
 
 
 def test_route_argument_validation(lib):
