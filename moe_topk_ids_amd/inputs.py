@@ -123,6 +123,28 @@ def make_biases(H: int, I: int, E: int, seed: int = 0) -> dict:
     return {"b1": b1.contiguous(), "b2": b2.contiguous()}
 
 
+def quantize_fp8_blocks(w: torch.Tensor, block: int):
+    """Synthetic sub-channel-quantised weights from bf16 weights [..., N, C]
+    (C the contraction axis): each run of `block` consecutive elements along
+    C gets the fp32 scale max|w| / 448, and the values w / scale are rounded
+    to OCP FP8 E4M3 (largest finite value 448). Returns (codes uint8
+    [..., N, C], scales fp32 [..., N, C/block])."""
+    *lead, n, c = w.shape
+    wb = w.float().reshape(*lead, n, c // block, block)
+    amax = wb.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (wb / scale).to(torch.float8_e4m3fn).reshape(*lead, n, c)
+    return q.view(torch.uint8).contiguous(), scale.squeeze(-1).contiguous()
+
+
+def make_fp8_weights(d: dict, block: int = 256) -> dict:
+    """FP8 E4M3 versions of an input set's w1 and w2 with per-block scales
+    along the contraction axis (H for w1, I for w2)."""
+    w1q, w1s = quantize_fp8_blocks(d["w1"], block)
+    w2q, w2s = quantize_fp8_blocks(d["w2"], block)
+    return {"w1q": w1q, "w1s": w1s, "w2q": w2q, "w2s": w2s, "block": block}
+
+
 def make_shape_inputs(name: str, seed: int = 0) -> dict:
     s = SHAPES[name]
     return make_inputs(s.T, s.H, s.I, s.E, s.K, seed=seed)

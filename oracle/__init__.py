@@ -52,6 +52,11 @@ def _load():
     lib.oracle_moe_forward_act_f64.restype = None
     lib.oracle_slot_act_bf16.argtypes = [p, p, p, i64, i64, i64, i64, i64, p]
     lib.oracle_slot_act_bf16.restype = None
+    lib.oracle_moe_forward_q.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, f32, f32, p, p, ctypes.c_int, p]
+    lib.oracle_moe_forward_q.restype = None
+    lib.oracle_fp8_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_to_f32.restype = ctypes.c_float
     lib.oracle_topk_softmax.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p]
     lib.oracle_topk_softmax.restype = None
     lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
@@ -174,6 +179,37 @@ def moe_forward_act_f64(x, w1, w2, topk_weights, topk_ids, act: str = "silu",
                                    K, ACTIVATIONS[act], alpha, limit, _optptr(b1), _optptr(b2),
                                    _ptr(out))
     return out
+
+
+def moe_forward_q(x, w1q, w1s, w2q, w2s, block: int, topk_weights, topk_ids, act: str = "silu",
+                  alpha: float = 1.702, limit: float = 7.0, b1=None, b2=None,
+                  bf16_inter: bool = False) -> np.ndarray:
+    """fp32 oracle forward with FP8 E4M3 weights (uint8 codes) and fp32
+    per-block scales: w1q [E,2I,H], w1s [E,2I,H/block], w2q [E,H,I],
+    w2s [E,H,I/block]."""
+    lib = _load()
+    x = _c(x, np.uint16)
+    w1q, w2q = _c(w1q, np.uint8), _c(w2q, np.uint8)
+    w1s, w2s = _c(w1s, np.float32), _c(w2s, np.float32)
+    tw, ids = _c(topk_weights, np.float32), _c(topk_ids, np.int32)
+    b1, b2 = _opt(b1, np.float32), _opt(b2, np.float32)
+    T, H = x.shape
+    E, I2, _ = w1q.shape
+    I = I2 // 2
+    K = ids.shape[1]
+    assert w1q.shape == (E, 2 * I, H) and w2q.shape == (E, H, I)
+    assert w1s.shape == (E, 2 * I, H // block) and w2s.shape == (E, H, I // block)
+    out = np.zeros((T, H), np.float32)
+    lib.oracle_moe_forward_q(_ptr(x), _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s), block,
+                             _ptr(tw), _ptr(ids), T, H, I, E, K, ACTIVATIONS[act], alpha, limit,
+                             _optptr(b1), _optptr(b2), 1 if bf16_inter else 0, _ptr(out))
+    return out
+
+
+def fp8_e4m3_to_f32(codes) -> np.ndarray:
+    lib = _load()
+    return np.array([lib.oracle_fp8_e4m3_to_f32(int(c)) for c in np.asarray(codes).ravel()],
+                    np.float32).reshape(np.shape(codes))
 
 
 def slot_act_bf16(x, w1, topk_ids) -> np.ndarray:

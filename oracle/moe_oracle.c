@@ -26,7 +26,12 @@
  *                limit 7 by default), and ref_moe's optional fp32 biases: b1
  *                added to the gate and up projections before the
  *                activation, b2 added to each expert's down projection
- *                before the routing weight.
+ *                before the routing weight. Its ref_moe also takes quantised
+ *                expert weights with per-block fp32 scales ("sub-channel"
+ *                quantisation): each weight is its quantised value, widened
+ *                to fp32, times the scale of its block of subc_quant_wsz
+ *                consecutive elements along the contraction axis, for its
+ *                own output column.
  *   [tpu-scatter] tpu-inference fused_moe v1 kernel.py, start_a2a_scatter:
  *                (token, k) pairs are placed into per-expert contiguous
  *                buffers by walking tokens in order and, inside a token, the
@@ -349,6 +354,89 @@ void oracle_moe_forward_f64(const uint16_t* x, const uint16_t* w1, const uint16_
                             int64_t H, int64_t I, int64_t E, int64_t K, double* out) {
   oracle_moe_forward_act_f64(x, w1, w2, topk_weights, topk_ids, T, H, I, E, K, ORA_ACT_SILU, 0.0,
                              0.0, NULL, NULL, out);
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantised expert weights ([tpu-v2] ref_moe with w1_scale/w2_scale)  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The quantised values are OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 mantissa bits, no infinities, 0x7F and 0xFF NaN, exponent
+ * field 0 for subnormals m * 2^-9. (The page leaves the quantised dtype
+ * open; this is the format the matrix and conversion units of the target
+ * read.)
+ */
+float oracle_fp8_e4m3_to_f32(uint8_t c) {
+  const int sgn = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+  float v;
+  if (ex == 15 && m == 7)
+    v = NAN;
+  else if (ex == 0)
+    v = ldexpf((float)m, -9);
+  else
+    v = ldexpf(1.0f + (float)m / 8.0f, ex - 7);
+  return sgn ? -v : v;
+}
+
+/*
+ * Forward with quantised weights, fp32 ([tpu-v2] ref_moe):
+ *   w1[e, n, h] = fp8(w1q[e, n, h]) * w1s[e, n, h / block]   (fp32 product)
+ *   w2[e, h, i] = fp8(w2q[e, h, i]) * w2s[e, h, i / block]
+ * then exactly oracle_moe_forward_act with those weights. Layouts: w1q uint8
+ * [E, 2I, H], w1s fp32 [E, 2I, H/block], w2q uint8 [E, H, I], w2s fp32
+ * [E, H, I/block]; block divides H and I.
+ */
+void oracle_moe_forward_q(const uint16_t* x, const uint8_t* w1q, const float* w1s,
+                          const uint8_t* w2q, const float* w2s, int64_t block,
+                          const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                          int64_t H, int64_t I, int64_t E, int64_t K, int act_kind, float alpha,
+                          float limit, const float* b1, const float* b2, int bf16_inter,
+                          float* out) {
+  float lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = oracle_fp8_e4m3_to_f32((uint8_t)c);
+  const int64_t nb1 = H / block, nb2 = I / block;
+#pragma omp parallel
+  {
+    float* act = (float*)malloc((size_t)I * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+      float* o = out + t * H;
+      for (int64_t h = 0; h < H; ++h) o[h] = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        const int32_t e = topk_ids[t * K + k];
+        if (e < 0 || e >= E) continue;
+        const float w = topk_weights[t * K + k];
+        for (int64_t i = 0; i < I; ++i) {
+          const int64_t rg = (int64_t)e * 2 * I + i, ru = rg + I;
+          float g = 0.0f, u = 0.0f;
+          for (int64_t h = 0; h < H; ++h) {
+            const float xv = ora_bf16_to_f32(x[t * H + h]);
+            const float wg = lut[w1q[rg * H + h]] * w1s[rg * nb1 + h / block];
+            const float wu = lut[w1q[ru * H + h]] * w1s[ru * nb1 + h / block];
+            g = g + xv * wg;
+            u = u + xv * wu;
+          }
+          if (b1) {
+            g = g + b1[(int64_t)e * 2 * I + i];
+            u = u + b1[(int64_t)e * 2 * I + I + i];
+          }
+          float a = ora_act_f32(g, u, act_kind, alpha, limit);
+          if (bf16_inter) a = ora_bf16_to_f32(ora_f32_to_bf16_rne(a));
+          act[i] = a;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+          const int64_t r = (int64_t)e * H + h;
+          float acc = 0.0f;
+          for (int64_t i = 0; i < I; ++i)
+            acc = acc + act[i] * (lut[w2q[r * I + i]] * w2s[r * nb2 + i / block]);
+          if (b2) acc = acc + b2[(int64_t)e * H + h];
+          o[h] = o[h] + w * acc;
+        }
+      }
+    }
+    free(act);
+  }
 }
 
 /* ------------------------------------------------------------------ */
