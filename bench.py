@@ -19,6 +19,7 @@ bounded sample of the same inputs, on this host's cores).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -29,7 +30,7 @@ import numpy as np
 import torch
 
 import moe_topk_ids_amd as moe
-from moe_topk_ids_amd.inputs import SHAPES, SHAPES_TABLE, bf16_bits, make_inputs
+from moe_topk_ids_amd.inputs import SHAPES, SHAPES_TABLE, bf16_bits, make_fp8_weights, make_inputs
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 METRIC = "fused-MoE bf16 TFLOP/s and µs/call per shape; % of MFMA/HBM roofline at 1 GPU"
@@ -133,13 +134,26 @@ def bench_router(args, s):
 
 
 def _time_forward(dev, copies, w1s, w2s, out, flags, steps, warmup):
-    """us per forward, rotating over the weight copies; HIP events."""
+    """us per forward, rotating over the weight copies; HIP events. The
+    timed calls go to the C ABI with pre-marshalled arguments (see main)."""
+    moe.moe_forward(dev["hidden_states"], w1s[0], w2s[0], dev["topk_weights"], dev["topk_ids"],
+                    out=out, flags=flags)  # checks shapes once
+    lib = moe.load_library()
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    T, H = dev["hidden_states"].shape
+    E, I2, _ = w1s[0].shape
+    K = dev["topk_ids"].shape[1]
+    argsets = [(P(dev["hidden_states"]), P(w1s[c]), P(w2s[c]), P(dev["topk_weights"]),
+                P(dev["topk_ids"]), T, H, I2 // 2, E, K, P(out), ctypes.c_uint32(flags or 0),
+                None, 0, ctypes.c_void_p(stream.cuda_stream)) for c in range(copies)]
+
     def step(i):
-        moe.moe_forward(dev["hidden_states"], w1s[i % copies], w2s[i % copies],
-                        dev["topk_weights"], dev["topk_ids"], out=out, flags=flags)
+        rc = lib.moe_forward_ex(*argsets[i % copies])
+        if rc != moe.MOE_OK:
+            raise moe.MoeError(rc, lib.moe_last_error().decode())
     for i in range(warmup):
         step(i)
-    stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -246,6 +260,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one weight copy every step")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="expert weights: bf16, or OCP FP8 E4M3 codes with an fp32 scale per "
+                         "block of 256 (128 where I is not a multiple of 256) along the "
+                         "contraction axis (moe_forward_fp8)")
     ap.add_argument("--stage", default="forward",
                     choices=["forward", "router", "copy", "table", "small_t"],
                     help="forward: the fused MoE forward (default); router: softmax/top-k "
@@ -285,16 +303,50 @@ def main():
     d = make_inputs(s.T, s.H, s.I, s.E, s.K, seed=0)
     dev = {k: v.cuda() for k, v in d.items()}
     touched = len(np.unique(d["topk_ids"].numpy()))
-    wbytes_touched = touched * 3 * s.H * s.I * 2
+    fp8 = args.weights == "fp8"
+    block = 256 if s.I % 256 == 0 else 128
+    wbytes_per_elem = 1 if fp8 else 2
+    wbytes_touched = touched * 3 * s.H * s.I * wbytes_per_elem
     copies = 1 if args.no_rotate else max(1, min(8, -(-512 * 2 ** 20 // wbytes_touched)))
-    w1s = [dev["w1"]] + [dev["w1"].clone() for _ in range(copies - 1)]
-    w2s = [dev["w2"]] + [dev["w2"].clone() for _ in range(copies - 1)]
     out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    # The timed loop calls the C ABI with its arguments marshalled once
+    # (the binding checks every tensor on each call, about 15 us of host
+    # time, which would hide the GPU time of the small-T paths). One call
+    # through the Python binding first checks the shapes and the result.
+    lib = moe.load_library()
+    cs = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    fl = ctypes.c_uint32(flags or 0)
+    if fp8:
+        q = make_fp8_weights(d, block)
+        qs = [{k: q[k].cuda() for k in ("w1q", "w1s", "w2q", "w2s")}]
+        qs += [{k: v.clone() for k, v in qs[0].items()} for _ in range(copies - 1)]
+        w1s = [torch.empty(0, device="cuda")] * copies  # unused on this path
+        w2s = w1s
+        flags = (flags or 0) | moe.FLAG_FP8_WEIGHTS
+        moe.moe_forward_fp8(dev["hidden_states"], qs[0]["w1q"], qs[0]["w1s"], qs[0]["w2q"],
+                            qs[0]["w2s"], block, dev["topk_weights"], dev["topk_ids"], out=out,
+                            flags=flags)
+        argsets = [(P(dev["hidden_states"]), P(c["w1q"]), P(c["w1s"]), P(c["w2q"]), P(c["w2s"]),
+                    block, P(dev["topk_weights"]), P(dev["topk_ids"]), s.T, s.H, s.I, s.E, s.K,
+                    moe.ACT_SILU, ctypes.c_float(1.702), ctypes.c_float(7.0), None, None, P(out),
+                    fl, None, 0, cs) for c in qs]
+        call = lib.moe_forward_fp8
+    else:
+        w1s = [dev["w1"]] + [dev["w1"].clone() for _ in range(copies - 1)]
+        w2s = [dev["w2"]] + [dev["w2"].clone() for _ in range(copies - 1)]
+        moe.moe_forward(dev["hidden_states"], w1s[0], w2s[0], dev["topk_weights"],
+                        dev["topk_ids"], out=out, flags=flags)
+        argsets = [(P(dev["hidden_states"]), P(w1s[c]), P(w2s[c]), P(dev["topk_weights"]),
+                    P(dev["topk_ids"]), s.T, s.H, s.I, s.E, s.K, P(out), fl, None, 0, cs)
+                   for c in range(copies)]
+        call = lib.moe_forward_ex
 
     def step(i):
-        moe.moe_forward(dev["hidden_states"], w1s[i % copies], w2s[i % copies],
-                        dev["topk_weights"], dev["topk_ids"], out=out, flags=flags)
+        rc = call(*argsets[i % copies])
+        if rc != moe.MOE_OK:
+            raise moe.MoeError(rc, lib.moe_last_error().decode())
 
     log(f"[bench] warmup {args.warmup} (weight copies: {copies})")
     for i in range(args.warmup):
@@ -317,15 +369,22 @@ def main():
     # ---- dominant kernel, timed on its own ----
     uses_decode = moe.moe_uses_decode_path(s.T, s.H, s.I, s.E, s.K, flags or 0)
     if uses_decode:
-        kernel = "decode_path"
-        alg_bytes = touched * 3 * s.H * s.I * 2 + s.T * s.H * 2 + s.T * s.H * 4 + s.T * s.K * 8
+        kernel = "decode_path_fp8" if fp8 else "decode_path"
+        scale_bytes = touched * 3 * s.H * (s.I // block) * 4 if fp8 else 0
+        alg_bytes = (touched * 3 * s.H * s.I * wbytes_per_elem + scale_bytes + s.T * s.H * 2
+                     + s.T * s.H * 4 + s.T * s.K * 8)
         dur_ms = ms_event
         achieved = alg_bytes / (dur_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "decode_gateup+decode_down (whole decode path)",
+        roof = {"bound": "hbm",
+                "kernel": ("decode_gateup_q+decode_down_q (whole decode path, fp8 weights)" if fp8
+                           else "decode_gateup+decode_down (whole decode path)"),
                 "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS,
                 "algorithmic_bytes": alg_bytes, "avg_launch_us": dur_ms * 1e3}
     else:
+        if fp8:  # the grouped path runs its GEMMs on the bf16-widened weights
+            w1s = [dev["w1"]]
+            copies = 1
         kernel = "grouped_gemm_gate_up_silu"
         M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
         r = moe.moe_route(dev["topk_ids"], s.E, M)
@@ -366,11 +425,11 @@ def main():
                         if args.workload in PAGE_T_PROD_US else None),
         "vs_baseline_note": ("page's production time on its own 'XPU-A' hardware for this "
                              "shapes-table row (context, not a target)"),
-        "dtype": "bf16",
+        "dtype": "bf16 (fp8-e4m3 expert weights)" if fp8 else "bf16",
         "data": "synthetic (seeded, atrex-bench #009 input recipe)",
         "config": {"workload": f"{s.name}: T={s.T} H={s.H} I={s.I} E={s.E} top_k={s.K}",
                    "T": s.T, "H": s.H, "I": s.I, "E": s.E, "top_k": s.K,
-                   "path": args.path, "weight_copies": copies,
+                   "path": args.path, "weights": args.weights, "weight_copies": copies,
                    "parallelism": "single GPU"},
         "roofline": roof,
     }

@@ -78,6 +78,10 @@ extern "C" {
 /* Force the expert-deduplicated small-batch path (each routed expert's rows
  * streamed once for all slots routed to it; T*K <= 1024). */
 #define MOE_FLAG_FORCE_SMALL_BATCH 32u
+/* For moe_workspace_bytes and moe_path: the sizes and path of
+ * moe_forward_fp8 (FP8 weights). moe_forward_fp8 sets it itself; the bf16
+ * entry points ignore it. */
+#define MOE_FLAG_FP8_WEIGHTS 64u
 
 /* Paths, as returned by moe_path. A FORCE flag whose path does not support
  * the sizes falls back to the grouped path. */
@@ -131,6 +135,31 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2,
  * this call with MOE_ACT_SILU and no biases.
  */
 int moe_forward_act(const void* hidden, const void* w1, const void* w2,
+                    const float* topk_weights, const int32_t* topk_ids,
+                    int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                    int32_t activation, float alpha, float limit,
+                    const float* b1, const float* b2,
+                    float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * As moe_forward_act, with expert weights quantised to OCP FP8 E4M3 (1 byte
+ * per weight: sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F and
+ * 0xFF are NaN) and one fp32 scale per `block` consecutive weights along the
+ * contraction axis (the sub-channel quantisation of the later tpu-inference
+ * fused_moe kernel.py, ref_moe's w1_scale and w2_scale):
+ *   w1q       uint8 [E, 2I, H]         w1[e,n,h] = fp8(w1q[e,n,h]) * w1_scale[e,n,h/block]
+ *   w1_scale  fp32  [E, 2I, H/block]
+ *   w2q       uint8 [E, H, I]          w2[e,h,i] = fp8(w2q[e,h,i]) * w2_scale[e,h,i/block]
+ *   w2_scale  fp32  [E, H, I/block]
+ * `block` must be a multiple of 128 dividing H and I (MOE_ERR_UNSUPPORTED
+ * otherwise). The per-token and small-batch paths read the codes directly;
+ * the grouped path widens all weights to bf16 in its workspace first (the
+ * fp32 product rounded to bf16), so its workspace holds a bf16 copy of w1 and
+ * w2: size it with moe_workspace_bytes(..., flags | MOE_FLAG_FP8_WEIGHTS).
+ */
+int moe_forward_fp8(const void* hidden, const uint8_t* w1q, const float* w1_scale,
+                    const uint8_t* w2q, const float* w2_scale, int64_t block,
                     const float* topk_weights, const int32_t* topk_ids,
                     int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
                     int32_t activation, float alpha, float limit,

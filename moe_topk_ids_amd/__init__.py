@@ -25,6 +25,7 @@ FLAG_FORCE_DECODE = 4
 FLAG_DEBUG_SYNC = 8
 FLAG_VALIDATE_IDS = 16
 FLAG_FORCE_SMALL_BATCH = 32
+FLAG_FP8_WEIGHTS = 64
 
 ACT_SILU = 0
 ACT_GELU_TANH = 1
@@ -69,6 +70,9 @@ def load_library():
     lib.moe_forward_act.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, f32, f32, p, p,
                                     p, u32, p, sz, p]
     lib.moe_forward_act.restype = ctypes.c_int
+    lib.moe_forward_fp8.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, i64, i32, f32,
+                                    f32, p, p, p, u32, p, sz, p]
+    lib.moe_forward_fp8.restype = ctypes.c_int
     lib.moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, u32]
     lib.moe_workspace_bytes.restype = sz
     lib.moe_m_tile.argtypes = [i64, i64, i64, i64, i64, u32]
@@ -189,6 +193,55 @@ def moe_forward(hidden_states, w1, w2, topk_weights, topk_ids, out=None, flags=N
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
         _check(lib.moe_forward_ex(*args, ctypes.c_uint32(flags or 0), ws_ptr,
                                   ctypes.c_size_t(ws_bytes), _stream(stream)))
+    return out
+
+
+def moe_forward_fp8(hidden_states, w1q, w1_scale, w2q, w2_scale, block, topk_weights, topk_ids,
+                    out=None, flags=0, workspace=None, stream=None, activation="silu",
+                    alpha=1.702, limit=7.0, b1=None, b2=None):
+    """The forward with FP8 E4M3 expert weights: uint8 codes w1q [E,2I,H] and
+    w2q [E,H,I] with fp32 scales w1_scale [E,2I,H/block], w2_scale
+    [E,H,I/block] (see moe_forward_fp8 in the header)."""
+    import torch
+
+    lib = load_library()
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(w1q, "w1q", torch.uint8, 3)
+    _need(w2q, "w2q", torch.uint8, 3)
+    _need(w1_scale, "w1_scale", torch.float32, 3)
+    _need(w2_scale, "w2_scale", torch.float32, 3)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, H = hidden_states.shape
+    E, I2, H1 = w1q.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    if H1 != H or tuple(w2q.shape) != (E, H, I) or block <= 0 or H % block or I % block \
+            or tuple(w1_scale.shape) != (E, 2 * I, H // block) \
+            or tuple(w2_scale.shape) != (E, H, I // block) \
+            or tuple(topk_weights.shape) != (T, K) or topk_ids.shape[0] != T:
+        raise ValueError("inconsistent shapes for the FP8 forward")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"unknown activation {activation!r}")
+    for b, name, shape in ((b1, "b1", (E, 2 * I)), (b2, "b2", (E, H))):
+        if b is not None:
+            _need(b, name, torch.float32, 2)
+            if tuple(b.shape) != shape:
+                raise ValueError(f"{name} must be {shape}")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=hidden_states.device)
+    else:
+        _need(out, "out", torch.float32, 2)
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    _check(lib.moe_forward_fp8(
+        _ptr(hidden_states), _ptr(w1q), _ptr(w1_scale), _ptr(w2q), _ptr(w2_scale), block,
+        _ptr(topk_weights), _ptr(topk_ids), T, H, I, E, K, ACTIVATIONS[activation],
+        ctypes.c_float(alpha), ctypes.c_float(limit), None if b1 is None else _ptr(b1),
+        None if b2 is None else _ptr(b2), _ptr(out), ctypes.c_uint32(flags or 0), ws_ptr,
+        ctypes.c_size_t(ws_bytes), _stream(stream)))
     return out
 
 

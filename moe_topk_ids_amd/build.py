@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_topk_ids.so")
 SOURCES = ["moe_api.hip", "route.hip", "gemm.hip", "combine.hip", "decode.hip", "small_batch.hip",
-           "router.hip"]
+           "fp8.hip", "router.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

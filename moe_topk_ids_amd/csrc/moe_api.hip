@@ -50,6 +50,7 @@ int hip_error(const char* what, hipError_t st) {
 constexpr double kSmallBatchUsPerWork = 1.4e-7;
 constexpr double kGroupedFixedUs = 60.0;
 constexpr double kGroupedUsPerWeightMB = 0.06;
+constexpr double kDequantBytesPerUs = 5.0e6;  // ~5 TB/s
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -82,8 +83,12 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
 }
 
 int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
-  const bool dec = moe::decode_supported(H, I, K);
-  const bool sb = moe::small_batch_supported(T, H, I, K);
+  // with FP8 weights the streaming paths move half the bytes and the
+  // grouped path first widens every expert's weights to bf16
+  const bool fp8 = (flags & MOE_FLAG_FP8_WEIGHTS) != 0;
+  const bool dec = fp8 ? moe::fp8_decode_supported(H, I, K) : moe::decode_supported(H, I, K);
+  const bool sb = fp8 ? moe::fp8_small_batch_supported(T, H, I, K)
+                      : moe::small_batch_supported(T, H, I, K);
   if ((flags & MOE_FLAG_FORCE_DECODE) && dec) return MOE_PATH_DECODE;
   if ((flags & MOE_FLAG_FORCE_SMALL_BATCH) && sb) return MOE_PATH_SMALL_BATCH;
   if (flags & (MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_SMALL_BATCH))
@@ -92,7 +97,9 @@ int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fl
   if (dec && slots <= std::max<int64_t>(K, E / 2)) return MOE_PATH_DECODE;
   const double routed_mb = (double)std::min<int64_t>(E, slots) * 6.0 * H * I / 1e6;
   const double sb_extra_us = kSmallBatchUsPerWork * (double)slots * H * I;
-  if (sb && sb_extra_us <= kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb)
+  // widening all E experts: 1 byte read and 2 written per weight
+  const double dequant_us = fp8 ? (double)E * 3.0 * H * I * 3.0 / kDequantBytesPerUs : 0.0;
+  if (sb && sb_extra_us <= kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb + dequant_us)
     return MOE_PATH_SMALL_BATCH;
   return MOE_PATH_GROUPED;
 }
@@ -107,6 +114,7 @@ struct Layout {
   bool decode = false;
   moe::GemmCfg g1{}, g2{};
   int64_t cap = 0, max_tiles = 0, nblk = 0;
+  size_t w1dq = 0, w2dq = 0;  // bf16 copies of FP8 weights (grouped path)
   size_t err = 0, counts = 0, offsets = 0, num_tiles = 0, tile_expert = 0, sorted = 0,
          slot_of = 0, block_hist = 0, act = 0, y = 0, total = 0;
 };
@@ -148,6 +156,10 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.block_hist = take((size_t)E * L.nblk * 4);
   L.act = take((size_t)L.cap * I * 2);
   if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)n * H * 4);
+  if (flags & MOE_FLAG_FP8_WEIGHTS) {
+    L.w1dq = take((size_t)E * 2 * I * H * 2);
+    L.w2dq = take((size_t)E * H * I * 2);
+  }
   L.total = p;
   return L;
 }
@@ -241,13 +253,27 @@ int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fla
   return pick_path(T, H, I, E, K, flags);
 }
 
-int moe_forward_act(const void* hidden, const void* w1, const void* w2,
-                    const float* topk_weights, const int32_t* topk_ids, int64_t T, int64_t H,
-                    int64_t I, int64_t E, int64_t K, int32_t activation, float alpha,
-                    float limit, const float* b1, const float* b2, float* out, uint32_t flags,
-                    void* workspace, size_t workspace_bytes, void* stream_ptr) {
+}  // extern "C"
+
+namespace {
+
+// The whole forward; `q` non-null means FP8 weights (w1/w2 unused).
+int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::Fp8Weights* q,
+                 const float* topk_weights, const int32_t* topk_ids, int64_t T, int64_t H,
+                 int64_t I, int64_t E, int64_t K, int32_t activation, float alpha, float limit,
+                 const float* b1, const float* b2, float* out, uint32_t flags, void* workspace,
+                 size_t workspace_bytes, void* stream_ptr) {
   int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
+  if (q) {
+    flags |= MOE_FLAG_FP8_WEIGHTS;
+    if (!moe::fp8_block_ok(H, I, q->block))
+      return set_error(MOE_ERR_UNSUPPORTED,
+                       "scale block %lld must be a multiple of 128 dividing H=%lld and I=%lld",
+                       (long long)q->block, (long long)H, (long long)I);
+  } else {
+    flags &= ~MOE_FLAG_FP8_WEIGHTS;
+  }
   if (activation < MOE_ACT_SILU || activation > MOE_ACT_GELU_ERF)
     return set_error(MOE_ERR_INVALID_ARG, "unknown activation %d", activation);
   if (activation == MOE_ACT_SWIGLUOAI && !(limit >= 0.0f && alpha == alpha))
@@ -259,7 +285,8 @@ int moe_forward_act(const void* hidden, const void* w1, const void* w2,
   ep.b1 = b1;
   ep.b2 = b2;
   if (T == 0) return MOE_OK;
-  if (!hidden || !w1 || !w2 || !topk_weights || !topk_ids || !out)
+  if (!hidden || !topk_weights || !topk_ids || !out ||
+      (q ? (!q->w1q || !q->w1s || !q->w2q || !q->w2s) : (!w1 || !w2)))
     return set_error(MOE_ERR_INVALID_ARG, "null device pointer with T=%lld", (long long)T);
   const Layout L = make_layout(T, H, I, E, K, flags);
   void* ws = workspace;
@@ -286,13 +313,19 @@ int moe_forward_act(const void* hidden, const void* w1, const void* w2,
   }
 
   if (L.decode) {
-    hipError_t st = moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
-                                       at<uint16_t>(ws, L.act), out, ep, stream);
+    hipError_t st =
+        q ? moe::launch_decode_fp8(x, *q, topk_weights, topk_ids, T, H, I, E, K,
+                                   at<uint16_t>(ws, L.act), out, ep, stream)
+          : moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
+                               at<uint16_t>(ws, L.act), out, ep, stream);
     if ((rc = stage_check(flags, "decode", st, stream)) != MOE_OK) return rc;
   } else if (L.path == MOE_PATH_SMALL_BATCH) {
     float* y = at<float>(ws, L.y);
-    hipError_t st = moe::launch_small_batch(x, wa, wb, topk_ids, T, H, I, E, K,
-                                            at<uint16_t>(ws, L.act), y, ep, stream);
+    hipError_t st =
+        q ? moe::launch_small_batch_fp8(x, *q, topk_ids, T, H, I, E, K, at<uint16_t>(ws, L.act),
+                                        y, ep, stream)
+          : moe::launch_small_batch(x, wa, wb, topk_ids, T, H, I, E, K, at<uint16_t>(ws, L.act),
+                                    y, ep, stream);
     if ((rc = stage_check(flags, "small_batch", st, stream)) != MOE_OK) return rc;
     st = moe::launch_combine(y, topk_weights, nullptr, topk_ids, E, T, H, K, ep.b2, out, stream);
     if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
@@ -305,7 +338,15 @@ int moe_forward_act(const void* hidden, const void* w1, const void* w2,
     int32_t* slot_of = at<int32_t>(ws, L.slot_of);
     int32_t* block_hist = at<int32_t>(ws, L.block_hist);
     uint16_t* act = at<uint16_t>(ws, L.act);
-    hipError_t st = moe::launch_route(topk_ids, T, K, E, L.g1.bm, block_hist, counts, offsets,
+    hipError_t st = hipSuccess;
+    if (q) {  // widen the FP8 weights to bf16 in the workspace
+      st = moe::launch_dequant_fp8(*q, E, H, I, at<uint16_t>(ws, L.w1dq),
+                                   at<uint16_t>(ws, L.w2dq), stream);
+      if ((rc = stage_check(flags, "dequant_fp8", st, stream)) != MOE_OK) return rc;
+      wa = at<uint16_t>(ws, L.w1dq);
+      wb = at<uint16_t>(ws, L.w2dq);
+    }
+    st = moe::launch_route(topk_ids, T, K, E, L.g1.bm, block_hist, counts, offsets,
                                       sorted, slot_of, tile_expert, num_tiles, stream);
     if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
     st = moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I, K,
@@ -339,6 +380,37 @@ int moe_forward_act(const void* hidden, const void* w1, const void* w2,
                        (long long)E);
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_act(const void* hidden, const void* w1, const void* w2,
+                    const float* topk_weights, const int32_t* topk_ids, int64_t T, int64_t H,
+                    int64_t I, int64_t E, int64_t K, int32_t activation, float alpha,
+                    float limit, const float* b1, const float* b2, float* out, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(hidden, w1, w2, nullptr, topk_weights, topk_ids, T, H, I, E, K,
+                      activation, alpha, limit, b1, b2, out, flags, workspace, workspace_bytes,
+                      stream);
+}
+
+int moe_forward_fp8(const void* hidden, const uint8_t* w1q, const float* w1_scale,
+                    const uint8_t* w2q, const float* w2_scale, int64_t block,
+                    const float* topk_weights, const int32_t* topk_ids, int64_t T, int64_t H,
+                    int64_t I, int64_t E, int64_t K, int32_t activation, float alpha,
+                    float limit, const float* b1, const float* b2, float* out, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  moe::Fp8Weights q;
+  q.w1q = w1q;
+  q.w1s = w1_scale;
+  q.w2q = w2q;
+  q.w2s = w2_scale;
+  q.block = block;
+  return forward_impl(hidden, nullptr, nullptr, &q, topk_weights, topk_ids, T, H, I, E, K,
+                      activation, alpha, limit, b1, b2, out, flags, workspace, workspace_bytes,
+                      stream);
 }
 
 int moe_forward_ex(const void* hidden, const void* w1, const void* w2, const float* topk_weights,

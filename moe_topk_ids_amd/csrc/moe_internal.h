@@ -85,6 +85,30 @@ hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const 
                               int64_t E, int64_t K, uint16_t* act, float* y,
                               const Epilogue& ep, hipStream_t stream);
 
+// Expert weights as OCP FP8 E4M3 codes with an fp32 scale per `block`
+// elements of the contraction axis (fp8.hip).
+struct Fp8Weights {
+  const uint8_t* w1q;  // [E, 2I, H]
+  const float* w1s;    // [E, 2I, H / block]
+  const uint8_t* w2q;  // [E, H, I]
+  const float* w2s;    // [E, H, I / block]
+  int64_t block;
+};
+bool fp8_block_ok(int64_t H, int64_t I, int64_t block);
+bool fp8_decode_supported(int64_t H, int64_t I, int64_t K);
+bool fp8_small_batch_supported(int64_t T, int64_t H, int64_t I, int64_t K);
+// Widen both weight tensors to bf16 (w1 [E, 2I, H], w2 [E, H, I]).
+hipError_t launch_dequant_fp8(const Fp8Weights& w, int64_t E, int64_t H, int64_t I,
+                              uint16_t* w1, uint16_t* w2, hipStream_t stream);
+hipError_t launch_decode_fp8(const uint16_t* hidden, const Fp8Weights& w,
+                             const float* topk_weights, const int32_t* topk_ids, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t K, uint16_t* act,
+                             float* out, const Epilogue& ep, hipStream_t stream);
+hipError_t launch_small_batch_fp8(const uint16_t* hidden, const Fp8Weights& w,
+                                  const int32_t* topk_ids, int64_t T, int64_t H, int64_t I,
+                                  int64_t E, int64_t K, uint16_t* act, float* y,
+                                  const Epilogue& ep, hipStream_t stream);
+
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int64_t K,
                                bool renormalize, float* weights, int32_t* ids,
                                hipStream_t stream);

@@ -30,7 +30,7 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
-              "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act"):
+              "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act", "moe_forward_fp8"):
         assert n in names
 
 
@@ -74,6 +74,25 @@ def test_activation_argument_validation(lib):
     for a in range(4):
         assert lib.moe_forward_act(p, p, p, p, p, 0, 128, 128, 8, 2, a, f(1.702), f(7.0), p, p, p,
                                    0, p, 0, p) == moe.MOE_OK
+
+
+def test_fp8_argument_validation(lib):
+    p = ctypes.c_void_p(0)
+    f = ctypes.c_float
+    # a scale block that is not a multiple of 128, or does not divide I
+    for block in (64, 200, 256):
+        rc = lib.moe_forward_fp8(p, p, p, p, p, block, p, p, 4, 512, 384, 8, 2, 0, f(1.702), f(7.0),
+                                 p, p, p, 0, p, 0, p)
+        assert rc == moe.MOE_ERR_UNSUPPORTED, block
+    # null weights with T > 0
+    assert lib.moe_forward_fp8(p, p, p, p, p, 128, p, p, 4, 512, 384, 8, 2, 0, f(1.702), f(7.0),
+                               p, p, p, 0, p, 0, p) == moe.MOE_ERR_INVALID_ARG
+    # the grouped path's workspace holds the bf16 copy of the weights
+    fl = moe.FLAG_FORCE_GROUPED
+    extra = (moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, fl | moe.FLAG_FP8_WEIGHTS)
+             - moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, fl))
+    assert extra >= 8 * 3 * 2048 * 2048 * 2
+    assert moe.moe_path(1, 2048, 768, 128, 8, moe.FLAG_FP8_WEIGHTS) == moe.PATH_DECODE
 
 
 def test_route_argument_validation(lib):
