@@ -128,6 +128,109 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Epilogue of one wave's WTM x WTN sub-tile (wave position wm, wn in the
+// tile): lane holds, for token row (lane & 31) of sub-tile tm, the weight
+// columns 8*j + 4*(lane >> 5) + {0,1,2,3} of sub-tile tn, in
+// acc[tn][tm][4j..4j+3].
+template <int BM, int BN, int WTM, int WTN, int MODE>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
+                                              f32x16_t (&acc)[WTN / 32][WTM / 32], int64_t m0,
+                                              int ntile, int e, int wm, int wn, int lane) {
+  constexpr int TM = WTM / 32;
+  constexpr int TN = WTN / 32;
+  const int csub = 4 * (lane >> 5);
+  if (MODE == kGateUpSilu) {
+    uint16_t* act = reinterpret_cast<uint16_t*>(args.out);
+    const int64_t n0g = (int64_t)ntile * (BN / 2);
+    if (args.act == kActSilu && args.bias == nullptr) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
+#pragma unroll
+        for (int tn = 0; tn < TN / 2; ++tn) {
+          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t& g = acc[tn][tm];
+            const f32x16_t& u = acc[tn + TN / 2][tm];
+            uint2 v;
+            v.x = pack_bf16x2(silu_mul(g[4 * j + 0], u[4 * j + 0]), silu_mul(g[4 * j + 1], u[4 * j + 1]));
+            v.y = pack_bf16x2(silu_mul(g[4 * j + 2], u[4 * j + 2]), silu_mul(g[4 * j + 3], u[4 * j + 3]));
+            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+          }
+        }
+      }
+    } else {  // activation variant and/or gate/up bias
+      const float* b1 = args.bias ? args.bias + (int64_t)e * 2 * args.inter : nullptr;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
+#pragma unroll
+        for (int tn = 0; tn < TN / 2; ++tn) {
+          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t& g = acc[tn][tm];
+            const f32x16_t& u = acc[tn + TN / 2][tm];
+            float a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float gv = g[4 * j + q], uv = u[4 * j + q];
+              if (b1) {
+                gv += b1[col + 8 * j + q];
+                uv += b1[args.inter + col + 8 * j + q];
+              }
+              a[q] = gated_act(gv, uv, args.act, args.alpha, args.limit);
+            }
+            uint2 v;
+            v.x = pack_bf16x2(a[0], a[1]);
+            v.y = pack_bf16x2(a[2], a[3]);
+            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+          }
+        }
+      }
+    }
+  } else {
+    float* dst = reinterpret_cast<float*>(args.out);
+    int32_t fr[TM];  // slot of each row, all looked up before the stores
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) fr[tm] = args.sorted[m0 + wm * WTM + tm * 32 + (lane & 31)];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int32_t f = fr[tm];
+      if (f < 0) continue;
+      float wgt = 1.0f;
+      int64_t orow;
+      if (MODE == kDownAtomic) {
+        wgt = args.topk_weights[f];
+        orow = (int64_t)(f / args.topk);
+      } else {
+        orow = f;
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int64_t col = (int64_t)ntile * BN + wn * WTN + tn * 32 + csub;
+        if (col >= args.n_out) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* p = dst + orow * args.n_out + col + 8 * j;
+          const f32x16_t& a = acc[tn][tm];
+          if (MODE == kDownSlot) {
+            *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+          } else if (args.bias == nullptr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * a[4 * j + i]);
+          } else {  // w * (y + b2[e]), the weight applied to the biased output
+            const float* b2 = args.bias + (int64_t)e * args.n_out + col + 8 * j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * (a[4 * j + i] + b2[i]));
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   constexpr int NW = WGM * WGN;
@@ -191,13 +294,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_num, 0x00020000);
   const __amdgpu_buffer_rsrc_t brsrc_b =
       __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_num, 0x00020000);
+  // token rows of the tile's slots: every lookup issued before the first
+  // use, offsets computed without branches
+  int32_t fsl[LA];
+#pragma unroll
+  for (int j = 0; j < LA; ++j)
+    fsl[j] = MODE == kGateUpSilu ? args.sorted[m0 + RPL * (wave * LA + j) + lane / CPR] : 0;
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     const int r = RPL * (wave * LA + j) + lane / CPR;
     const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(r)) * 16);
     if (MODE == kGateUpSilu) {
-      const int32_t f = args.sorted[m0 + r];
-      aoff[j] = f >= 0 ? (uint32_t)((int64_t)(f / args.topk) * kdim * 2) + cb : kOutOfRange;
+      const int32_t f = fsl[j];
+      const uint32_t t = (uint32_t)(f >= 0 ? f : 0) / (uint32_t)args.topk;
+      aoff[j] = f >= 0 ? t * (uint32_t)(kdim * 2) + cb : kOutOfRange;
     } else {
       aoff[j] = (uint32_t)(r * kdim * 2) + cb;
     }
@@ -388,98 +498,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
-  // ---- epilogues ----
-  // lane holds, for token row (lane & 31) of sub-tile tm, the weight columns
-  // 8*j + 4*(lane >> 5) + {0,1,2,3} of sub-tile tn, in acc[tn][tm][4j..4j+3]
-  const int csub = 4 * (lane >> 5);
-  if (MODE == kGateUpSilu) {
-    uint16_t* act = reinterpret_cast<uint16_t*>(args.out);
-    const int64_t n0g = (int64_t)ntile * (BN / 2);
-    if (args.act == kActSilu && args.bias == nullptr) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn) {
-          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x16_t& g = acc[tn][tm];
-            const f32x16_t& u = acc[tn + TN / 2][tm];
-            uint2 v;
-            v.x = pack_bf16x2(silu_mul(g[4 * j + 0], u[4 * j + 0]), silu_mul(g[4 * j + 1], u[4 * j + 1]));
-            v.y = pack_bf16x2(silu_mul(g[4 * j + 2], u[4 * j + 2]), silu_mul(g[4 * j + 3], u[4 * j + 3]));
-            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
-          }
-        }
-      }
-    } else {  // activation variant and/or gate/up bias
-      const float* b1 = args.bias ? args.bias + (int64_t)e * 2 * args.inter : nullptr;
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn) {
-          const int64_t col = n0g + wn * (WTN / 2) + tn * 32 + csub;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x16_t& g = acc[tn][tm];
-            const f32x16_t& u = acc[tn + TN / 2][tm];
-            float a[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float gv = g[4 * j + q], uv = u[4 * j + q];
-              if (b1) {
-                gv += b1[col + 8 * j + q];
-                uv += b1[args.inter + col + 8 * j + q];
-              }
-              a[q] = gated_act(gv, uv, args.act, args.alpha, args.limit);
-            }
-            uint2 v;
-            v.x = pack_bf16x2(a[0], a[1]);
-            v.y = pack_bf16x2(a[2], a[3]);
-            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
-          }
-        }
-      }
-    }
-  } else {
-    float* dst = reinterpret_cast<float*>(args.out);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int64_t r = m0 + wm * WTM + tm * 32 + (lane & 31);
-      const int32_t f = args.sorted[r];
-      if (f < 0) continue;
-      float wgt = 1.0f;
-      int64_t orow;
-      if (MODE == kDownAtomic) {
-        wgt = args.topk_weights[f];
-        orow = (int64_t)(f / args.topk);
-      } else {
-        orow = f;
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int64_t col = (int64_t)ntile * BN + wn * WTN + tn * 32 + csub;
-        if (col >= args.n_out) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float* p = dst + orow * args.n_out + col + 8 * j;
-          const f32x16_t& a = acc[tn][tm];
-          if (MODE == kDownSlot) {
-            *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
-          } else if (args.bias == nullptr) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * a[4 * j + i]);
-          } else {  // w * (y + b2[e]), the weight applied to the biased output
-            const float* b2 = args.bias + (int64_t)e * args.n_out + col + 8 * j;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(p + i, wgt * (a[4 * j + i] + b2[i]));
-          }
-        }
-      }
-    }
-  }
+  tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
