@@ -93,7 +93,10 @@ extern "C" {
  * The fused forward: out = sum_k topk_weights[:,k] * Expert_{topk_ids[:,k]}(hidden).
  * Uses a per-device workspace that the library allocates on first use and
  * grows as needed (freed by moe_release); the first call for a new maximum
- * size allocates and is therefore not graph-capture safe. The combine mode
+ * size allocates and is therefore not graph-capture safe. Calls that use the
+ * internal workspace of one device share it: they must be ordered (one
+ * stream, or synchronised), else give each concurrent caller its own
+ * workspace through moe_forward_ex. The combine mode
  * comes from the environment variable MOE_COMBINE ("slot", the default, or
  * "atomic"), read once.
  */
