@@ -341,3 +341,41 @@ def test_single_hip_runtime_is_mapped():
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
     assert any("libmoe_topk_ids.so" in line for line in maps.splitlines())
+
+
+@pytest.mark.parametrize("T,H,I,E,K", [
+    (64, 128, 128, 1024, 8),    # the largest expert count
+    (33, 128, 256, 1, 1),       # one expert, top-1
+    (5, 8192, 128, 16, 4),      # the largest hidden size the per-token path holds
+    (3, 256, 8192, 8, 2),       # a wide intermediate on every path
+])
+@pytest.mark.parametrize("path", ["default", "slot", "atomic", "decode", "small_batch"])
+def test_extreme_sizes(T, H, I, E, K, path):
+    require_gpu()
+    d = cpu_inputs(T, H, I, E, K, seed=T + H)
+    dd = to_device(d)
+    say(f"extreme T={T} H={H} I={I} E={E} K={K} path={path}")
+    got = _run(dd, None if path == "default" else PATHS[path])
+    rows = np.arange(T)
+    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"extreme {T},{H},{I},{E},{K}/{path}")
+
+
+def test_binding_rejects_bad_tensors():
+    require_gpu()
+    dd = to_device(shape_inputs("tiny"))
+    with pytest.raises(ValueError):  # not contiguous
+        moe.moe_forward(dd["hidden_states"].t().contiguous().t(), dd["w1"], dd["w2"],
+                        dd["topk_weights"], dd["topk_ids"])
+    with pytest.raises(ValueError):  # wrong dtype
+        moe.moe_forward(dd["hidden_states"].float(), dd["w1"], dd["w2"], dd["topk_weights"],
+                        dd["topk_ids"])
+    with pytest.raises(ValueError):  # host tensor
+        moe.moe_forward(dd["hidden_states"].cpu(), dd["w1"], dd["w2"], dd["topk_weights"],
+                        dd["topk_ids"])
+    with pytest.raises(ValueError):  # inconsistent shapes
+        moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"][:, :, :-128].contiguous(),
+                        dd["topk_weights"], dd["topk_ids"])
+    with pytest.raises(ValueError):  # unknown activation
+        moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                        dd["topk_ids"], activation="relu")
