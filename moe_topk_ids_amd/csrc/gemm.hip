@@ -523,16 +523,65 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
 
 }  // namespace
 
-// Row tile from the mean number of rows per routed expert: big tiles reuse
-// each staged byte more, small tiles waste fewer pad rows.
-GemmCfg pick_gemm1_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E) {
-  (void)H;
-  (void)I;
-  const int64_t live = n_slots < E ? n_slots : E;
-  const int64_t rows_per_expert = live > 0 ? n_slots / live : 0;
-  if (rows_per_expert >= 2048) return GemmCfg{256, 256};
-  if (rows_per_expert >= 96) return GemmCfg{128, 128};
-  return GemmCfg{64, 256};
+// Tile choice from a cost model of the two grouped products.
+//
+// Expected row tiles: with K distinct experts drawn per token, an expert's
+// row count is binomial (mean T*K/E, variance T*(K/E)*(1-K/E)); the expected
+// number of BM-row tiles it needs is averaged over five points of the
+// normal approximation. A product's time is then taken as (tiles per CU) x
+// (flops per tile) / (relative tile efficiency). 64x256 and 128x128 tiles
+// run two workgroups per CU, so their tail rounds overlap and the count
+// stays fractional; a 256x256 tile fills a CU alone, so it is rounded up to
+// whole rounds. The efficiencies (64x256 0.91, 128x128 1, 256x256 1.23)
+// were fitted to measured times of all three configurations on every shape
+// of the atrex-bench shapes table; against the fastest configuration per
+// shape the model gives up at most 1-2 % except in the weight-streaming
+// corner (E=128, I=384, ~32 rows per expert), where 128x128 is 10 % faster.
+namespace {
+double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
+  const int64_t n = T * K;
+  const double live = (double)(n < E ? n : E);
+  const double mean = (double)n / live;
+  const double p = (double)K / (double)E;
+  const double sd = sqrt((double)T * p * (1.0 - p));
+  const double z[5] = {-2.0, -1.0, 0.0, 1.0, 2.0};
+  const double w[5] = {0.054, 0.242, 0.399, 0.242, 0.054};
+  double acc = 0.0, wsum = 0.0;
+  for (int i = 0; i < 5; ++i) {
+    const double rows = fmax(1.0, mean + z[i] * sd);
+    acc += w[i] * ceil(rows / bm);
+    wsum += w[i];
+  }
+  return live * acc / wsum;
+}
+
+double model_cost(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E, GemmCfg c) {
+  const double eff = c.bm == 64 ? 0.91 : c.bm == 128 ? 1.0 : 1.23;
+  const double rt = expected_row_tiles(T, K, E, c.bm);
+  const double prod[2][2] = {{(double)H, (double)(2 * I / c.bn)},                  // gate/up
+                             {(double)I, (double)((H + c.bn - 1) / c.bn)}};  // down
+  double t = 0.0;
+  for (int g = 0; g < 2; ++g) {
+    const double per_cu = rt * prod[g][1] / 256.0;
+    const double rounds = c.bm == 256 ? fmax(1.0, ceil(per_cu - 0.02)) : fmax(1.0, per_cu);
+    t += rounds * (double)c.bm * c.bn * prod[g][0] * 2.0 / eff;
+  }
+  return t;
+}
+}  // namespace
+
+GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
+  const GemmCfg cands[3] = {{64, 256}, {128, 128}, {256, 256}};
+  GemmCfg best = cands[1];
+  double best_t = model_cost(T, K, H, I, E, best);
+  for (const GemmCfg& c : cands) {
+    const double t = model_cost(T, K, H, I, E, c);
+    if (t < best_t) {
+      best = c;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm) {

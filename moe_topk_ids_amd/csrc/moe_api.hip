@@ -142,7 +142,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
     L.total = p;
     return L;
   }
-  L.g1 = moe::pick_gemm1_cfg(n, H, I, E);
+  L.g1 = moe::pick_gemm1_cfg(T, K, H, I, E);
   L.g2 = moe::pick_gemm2_cfg(n, H, I, E, L.g1.bm);
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
@@ -238,7 +238,7 @@ int32_t moe_m_tile(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   (void)flags;
   const int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  return moe::pick_gemm1_cfg(T * K, H, I, E).bm;
+  return moe::pick_gemm1_cfg(T, K, H, I, E).bm;
 }
 
 int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {

@@ -44,7 +44,7 @@ struct GemmCfg {
   int bn;  // weight rows per tile (GEMM1: half gate, half up)
 };
 
-GemmCfg pick_gemm1_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E);
+GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E);
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm);
 
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,

@@ -126,6 +126,16 @@ def test_workspace_and_tile_queries(lib):
         moe.moe_m_tile(1, 100, 128, 8, 2)
 
 
+def test_tile_choice(lib):
+    # the cost model's picks on shapes where the measured winner is clear
+    assert moe.moe_m_tile(135, 2048, 2048, 8, 2) == 128    # few rows: more tiles in flight
+    assert moe.moe_m_tile(668, 2048, 2048, 8, 2) == 64     # ~167 rows per expert: least padding
+    assert moe.moe_m_tile(2400, 2048, 768, 128, 8) == 64
+    assert moe.moe_m_tile(8192, 4096, 384, 128, 8) == 256  # many tiles: the big tile's efficiency
+    assert moe.moe_m_tile(15381, 4096, 4096, 8, 2) == 256
+    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128)  # 256-row tiles leave a tail round
+
+
 def test_path_choice(lib):
     assert moe.moe_path(1, 2048, 768, 128, 8) == moe.PATH_DECODE
     assert moe.moe_path(4195, 2048, 2048, 8, 2) == moe.PATH_GROUPED
