@@ -12,6 +12,9 @@ namespace moe {
 // Slots handled by one routing workgroup (grows with T*K so that the number
 // of routing workgroups stays at most kRouteMaxBlocks).
 constexpr int kRouteThreads = 256;
+// Problems up to this size are routed by one workgroup in one launch.
+constexpr int64_t kRouteSingleMaxSlots = 32768;
+constexpr int64_t kRouteSingleMaxExperts = 512;
 constexpr int kRouteMaxBlocks = 128;
 constexpr int kMaxExperts = 1024;
 

@@ -3,7 +3,12 @@
 // kernel (kernel.py, start_a2a_scatter) fills its per-expert buffers, and
 // pads every expert's group to the GEMM row tile.
 //
-// Two launches, no atomics on the ordering path:
+// Up to kRouteSingleMaxSlots slots (and kRouteSingleMaxExperts experts) one
+// workgroup of 16 waves does everything in a single launch (route_single):
+// the whole problem is a few hundred KB of ids, so the cost is the launch,
+// and a second launch plus a global histogram pass would double it.
+//
+// Above that, two launches, no atomics on the ordering path:
 //   route_count    per workgroup, a per-expert histogram of its slot range
 //                  (LDS atomics: counts do not depend on order);
 //   route_scatter  every workgroup rebuilds the prefix sums it needs from the
@@ -11,6 +16,10 @@
 //                  wave ballots so equal experts keep ascending slot order.
 // Workgroup 0 publishes counts/offsets/num_tiles; pad rows and the
 // tile->expert map are spread over the workgroups by expert.
+//
+// Both forms rank slots the same way: each wave owns a contiguous, ordered
+// range of slots, waves are ordered by range, and inside a wave a 64-slot
+// chunk is ranked by ballot with the lowest lane first.
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,6 +49,39 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(
 __device__ inline uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+constexpr int kSingleThreads = 1024;
+constexpr int kSingleWaves = kSingleThreads / 64;
+
+__device__ inline void rank_and_scatter(const int32_t* __restrict__ ids, int64_t n_slots,
+                                        int32_t E, int64_t wbase, int64_t per_wave,
+                                        int32_t* myrun, int32_t* __restrict__ sorted,
+                                        int32_t* __restrict__ slot_of) {
+  const int lane = threadIdx.x & 63;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int64_t c0 = 0; c0 < per_wave; c0 += 64) {
+    const int64_t f = wbase + c0 + lane;
+    const bool in = (c0 + lane < per_wave) && (f < n_slots);
+    const int32_t e = in ? ids[f] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t bm = __ballot(set);
+      mask &= set ? bm : ~bm;
+    }
+    if (valid) {
+      const int32_t rank = __popcll(mask & lanemask_lt());
+      const int32_t pos = myrun[e] + rank;
+      sorted[pos] = (int32_t)f;
+      slot_of[f] = pos;
+      if (rank == 0) myrun[e] = pos + __popcll(mask);
+    } else if (in) {
+      slot_of[f] = -1;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scatter(
@@ -134,29 +176,87 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
 
   // 5. stable scatter: chunks of 64 slots in order; rank among equal ids by
   //    ballot, lowest lane first
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  for (int64_t c0 = 0; c0 < per_wave; c0 += 64) {
-    const int64_t f = wbase + c0 + lane;
-    const bool in = (c0 + lane < per_wave) && (f < n_slots);
-    const int32_t e = in ? ids[f] : -1;
-    const bool valid = in && e >= 0 && e < E;
-    uint64_t mask = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((e >> bit) & 1);
-      const uint64_t bm = __ballot(set);
-      mask &= set ? bm : ~bm;
-    }
-    if (valid) {
-      const int32_t rank = __popcll(mask & lanemask_lt());
-      const int32_t pos = myrun[e] + rank;
-      sorted[pos] = (int32_t)f;
-      slot_of[f] = pos;
-      if (rank == 0) myrun[e] = pos + __popcll(mask);
-    } else if (in) {
-      slot_of[f] = -1;
-    }
+  rank_and_scatter(ids, n_slots, E, wbase, per_wave, myrun, sorted, slot_of);
+}
+
+__global__ __launch_bounds__(kSingleThreads) void route_single(
+    const int32_t* __restrict__ ids, int64_t n_slots, int32_t E, int32_t M,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ num_tiles) {
+  // LDS: run[kSingleWaves][E] (per-wave counts, then each wave's first row
+  // per expert), tot[E], off[E+1]
+  extern __shared__ int32_t lds[];
+  int32_t* run = lds;
+  int32_t* tot = run + kSingleWaves * E;
+  int32_t* off = tot + E;
+  __shared__ int32_t part[kSingleThreads];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+
+  for (int i = tid; i < kSingleWaves * E; i += kSingleThreads) run[i] = 0;
+  __syncthreads();
+
+  // 1. per-wave counts over contiguous, 64-aligned slot ranges
+  const int64_t per_wave = ((n_slots + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
+  const int64_t wbase = (int64_t)wave * per_wave;
+  int32_t* myrun = run + wave * E;
+  for (int64_t i = lane; i < per_wave; i += 64) {
+    const int64_t f = wbase + i;
+    if (f >= n_slots) break;
+    const int32_t e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&myrun[e], 1);
   }
+  __syncthreads();
+
+  // 2. per expert: total, and each wave's exclusive prefix inside the expert
+  for (int e = tid; e < E; e += kSingleThreads) {
+    int32_t a = 0;
+    for (int w = 0; w < kSingleWaves; ++w) {
+      const int32_t c = run[w * E + e];
+      run[w * E + e] = a;
+      a += c;
+    }
+    tot[e] = a;
+  }
+  __syncthreads();
+
+  // 3. exclusive scan over experts of the padded counts
+  const int per = (E + kSingleThreads - 1) / kSingleThreads;
+  const int e0 = tid * per;
+  int32_t local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) local += (tot[e] + M - 1) / M * M;
+  part[tid] = local;
+  __syncthreads();
+  for (int d = 1; d < kSingleThreads; d <<= 1) {
+    const int32_t v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[tid] - local;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    off[e] = acc;
+    acc += (tot[e] + M - 1) / M * M;
+  }
+  if (tid == kSingleThreads - 1) off[E] = part[tid];
+  __syncthreads();
+
+  // 4. metadata, pad rows, tile->expert map; waves' absolute first rows
+  for (int e = tid; e < E; e += kSingleThreads) counts[e] = tot[e];
+  for (int e = tid; e <= E; e += kSingleThreads) offsets[e] = off[e];
+  if (tid == 0) num_tiles[0] = off[E] / M;
+  for (int e = wave; e < E; e += kSingleWaves) {
+    const int32_t start = off[e], padded = off[e + 1] - off[e];
+    for (int32_t j = lane; j < padded / M; j += 64) tile_expert[start / M + j] = (int32_t)e;
+    for (int32_t r = tot[e] + lane; r < padded; r += 64) sorted[start + r] = -1;
+  }
+  for (int i = tid; i < kSingleWaves * E; i += kSingleThreads) run[i] += off[i % E];
+  __syncthreads();
+
+  // 5. stable scatter
+  rank_and_scatter(ids, n_slots, E, wbase, per_wave, myrun, sorted, slot_of);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void validate_ids(const int32_t* __restrict__ ids,
@@ -185,9 +285,15 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int
                         int32_t* block_hist, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
                         int32_t* tile_expert, int32_t* num_tiles, hipStream_t stream) {
   const int64_t n = T * K;
+  if (n == 0) return hipSuccess;
+  if (n <= kRouteSingleMaxSlots && E <= kRouteSingleMaxExperts) {
+    const size_t lds = (size_t)(kSingleWaves * E + E + E + 1) * sizeof(int32_t);
+    route_single<<<dim3(1), dim3(kSingleThreads), lds, stream>>>(
+        ids, n, (int32_t)E, m_tile, counts, offsets, sorted, slot_of, tile_expert, num_tiles);
+    return hipGetLastError();
+  }
   const int64_t rb = route_block_slots(n);
   const int64_t nblk = route_blocks(n);
-  if (nblk == 0) return hipSuccess;
   route_count<<<dim3((unsigned)nblk), dim3(kRouteThreads), E * sizeof(int32_t), stream>>>(
       ids, n, (int32_t)E, rb, block_hist);
   hipError_t st = hipGetLastError();

@@ -47,7 +47,9 @@ def _rand_ids(T, K, E, seed):
 
 @pytest.mark.parametrize("case", ["one_expert", "empty_experts", "single_token_e128",
                                   "ragged_multiblock", "k_equals_e", "out_of_range",
-                                  "many_blocks", "m16", "m256"])
+                                  "many_blocks", "m16", "m256", "single_wg_limit",
+                                  "multi_wg_just_past", "multi_wg_out_of_range",
+                                  "multi_wg_e1024"])
 def test_route_edge_cases(case):
     require_gpu()
     rng = np.random.default_rng(7)
@@ -70,6 +72,17 @@ def test_route_edge_cases(case):
         ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = -3
         ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = 16
         _check_route(ids, 16, 64, case)
+    elif case == "single_wg_limit":  # 32768 slots, 512 experts: the one-workgroup form's limit
+        _check_route(_rand_ids(4096, 8, 512, 12), 512, 64, case)
+    elif case == "multi_wg_just_past":  # 32776 slots: the two-launch form
+        _check_route(_rand_ids(4097, 8, 64, 13), 64, 128, case)
+    elif case == "multi_wg_out_of_range":
+        ids = _rand_ids(5000, 8, 64, 14)
+        ids[rng.integers(0, 5000, 200), rng.integers(0, 8, 200)] = -1
+        ids[rng.integers(0, 5000, 200), rng.integers(0, 8, 200)] = 64
+        _check_route(ids, 64, 64, case)
+    elif case == "multi_wg_e1024":  # few slots, more experts than the one-workgroup form takes
+        _check_route(_rand_ids(100, 8, 1024, 15), 1024, 128, case)
     elif case == "many_blocks":  # the largest workload row on the shapes table
         _check_route(_rand_ids(45936, 8, 128, 8), 128, 128, case)
     elif case == "m16":
