@@ -44,6 +44,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 
 enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2 };
@@ -70,6 +71,12 @@ struct GemmArgs {
   int32_t act;
   float alpha, limit;
   const float* bias;
+  // fp8 weights (instead of w): codes [E, rows, kdim] and one fp32 scale per
+  // qblock codes along the contraction, [E, rows, nqb]
+  const uint8_t* wq;
+  const float* wscale;
+  int32_t qblock;
+  int32_t nqb;
 };
 
 // XOR permutation of the 16-byte chunks of a staged row (CPR chunks per
@@ -118,6 +125,34 @@ __device__ __forceinline__ void load_lds_b128(int32x4_t rsrc, uint32_t voffset, 
       :
       : "s"(lds_addr), "v"(voffset), "s"(rsrc)
       : "memory", "m0");
+}
+
+// One 4-byte load per lane into LDS: lane i's word lands at lds_addr + 4*i.
+__device__ __forceinline__ void load_lds_b32(int32x4_t rsrc, uint32_t voffset, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// 8 OCP E4M3 codes (k order: the bytes of lo, then of hi) to bf16 as
+// bf16_rne(fp32(code) * scale): the decode is exact, the product is the fp32
+// one, then one rounding to bf16.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi, float scale) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+  const float c0 = c[0], c1 = c[1], d0 = d[0], d1 = d[1];
+  u32x4_t v;
+  v[0] = pack_bf16x2(a0 * scale, a1 * scale);
+  v[1] = pack_bf16x2(b0 * scale, b1 * scale);
+  v[2] = pack_bf16x2(c0 * scale, c1 * scale);
+  v[3] = pack_bf16x2(d0 * scale, d1 * scale);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
@@ -231,27 +266,34 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
   }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE, bool Q>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;  // token rows per wave
   constexpr int WTN = BN / WGN;  // weight rows per wave
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int ROWB = BK * 2;       // bytes per staged row
-  constexpr int CPR = ROWB / 16;     // 16-byte chunks per staged row
-  constexpr int RPL = 1024 / ROWB;   // staged rows per 1 KB wave load
-  constexpr int LA = BM / (RPL * NW);  // 1 KB token-row loads per wave per stage
-  constexpr int LB = BN / (RPL * NW);  // 1 KB weight-row loads per wave per stage
+  constexpr int ROWB = BK * 2;            // bytes per staged token row
+  constexpr int ROWW = Q ? BK : BK * 2;   // bytes per staged weight row (fp8 or bf16)
+  constexpr int CPR = ROWB / 16;          // 16-byte chunks per staged row
+  constexpr int CPW = ROWW / 16;
+  constexpr int RPL = 1024 / ROWB;        // staged rows per 1 KB wave load
+  constexpr int RPW = 1024 / ROWW;
+  constexpr int LA = BM / (RPL * NW);     // 1 KB token-row loads per wave per stage
+  constexpr int LB = BN / (RPW * NW);     // 1 KB weight-row loads per wave per stage
   static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(!Q || BK == 64, "fp8 weights are staged 64 codes per row");
   constexpr int A_BYTES = BM * ROWB;
-  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int STAGE = BM * ROWB + BN * ROWW;
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 1, "tile too small");
   static_assert(MODE != kGateUpSilu || (TN % 2 == 0), "gate/up pairing needs even TN");
   static_assert(NS >= 2, "at least two stages");
-  static_assert(P == 0 || NS == 2, "register staging uses a two-buffer LDS ring");
 
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  // fp8 weights: the tile's per-block scales in dynamic LDS, [BN][nqb | 1]
+  // (odd row stride: 32 consecutive rows read at one block hit distinct
+  // banks), plus the overhang of the last 64-word load
+  extern __shared__ __attribute__((aligned(256))) float scl[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,6 +321,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int64_t m0 = (int64_t)mt * BM;
   const int64_t kdim = args.kdim;
 
+  // weight row (within the expert) of staged row n of this tile, or -1
+  auto weight_row = [&](int n) -> int64_t {
+    if (MODE == kGateUpSilu) {
+      const int64_t n0g = (int64_t)ntile * (BN / 2);
+      return n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
+    }
+    const int64_t row = (int64_t)ntile * BN + n;
+    return row < args.n_out ? row : -1;
+  };
+
   // ---- per-lane load offsets (fixed over the K loop) ----
   // load j of this wave covers staged rows RPL*g .. RPL*g+RPL-1 (g = wave*L
   // + j); lane -> row RPL*g + lane/CPR, physical chunk lane%CPR, logical
@@ -286,14 +338,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   uint32_t aoff[LA], boff[LB];
   const uint16_t* a_base = MODE == kGateUpSilu ? args.a : args.a + m0 * kdim;
   const uint32_t a_num = MODE == kGateUpSilu ? args.a_bytes : (uint32_t)(BM * kdim * 2);
-  const uint16_t* b_base = args.w + (int64_t)e * args.w_expert_stride;
-  const uint32_t b_num = (uint32_t)(args.w_expert_stride * 2);
+  const char* b_base = Q ? reinterpret_cast<const char*>(args.wq) + (int64_t)e * args.w_expert_stride
+                         : reinterpret_cast<const char*>(args.w + (int64_t)e * args.w_expert_stride);
+  const uint32_t b_num = (uint32_t)(args.w_expert_stride * (Q ? 1 : 2));
   const int32x4_t rsrc_a = make_rsrc(a_base, a_num);
   const int32x4_t rsrc_b = make_rsrc(b_base, b_num);
-  const __amdgpu_buffer_rsrc_t brsrc_a =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_num, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brsrc_b =
-      __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_num, 0x00020000);
   // token rows of the tile's slots: every lookup issued before the first
   // use, offsets computed without branches
   int32_t fsl[LA];
@@ -314,18 +363,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int n = RPL * (wave * LB + j) + lane / CPR;
-    const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(n)) * 16);
-    if (MODE == kGateUpSilu) {
-      const int64_t n0g = (int64_t)ntile * (BN / 2);
-      const int64_t row = n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
-      boff[j] = (uint32_t)(row * kdim * 2) + cb;
-    } else {
-      const int64_t row = (int64_t)ntile * BN + n;
-      boff[j] = row < args.n_out ? (uint32_t)(row * kdim * 2) + cb : kOutOfRange;
-    }
+    const int n = RPW * (wave * LB + j) + lane / CPW;
+    const uint32_t cb = (uint32_t)(((lane % CPW) ^ swz<CPW>(n)) * 16);
+    const int64_t row = weight_row(n);
+    boff[j] = row >= 0 ? (uint32_t)(row * kdim * (Q ? 1 : 2)) + cb : kOutOfRange;
   }
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+
+  // fp8 weights: the tile's scales go to LDS ahead of stage 0's loads (and
+  // so have landed once stage 0 has: loads complete in issue order)
+  int sst = 1;
+  if constexpr (Q) {
+    const int nqb = args.nqb;
+    sst = nqb | 1;
+    const int64_t rows_pe = args.w_expert_stride / kdim;
+    const int32x4_t rsrc_s =
+        make_rsrc(args.wscale + (int64_t)e * rows_pe * nqb, (uint32_t)(rows_pe * nqb * 4));
+    const uint32_t scl_base = (uint32_t)reinterpret_cast<uintptr_t>(scl);
+    for (int p0 = wave * 64; p0 < BN * sst; p0 += NW * 64) {
+      const int p = p0 + lane;
+      const int n = p / sst, b = p - n * sst;
+      const int64_t row = n < BN ? weight_row(n) : -1;
+      const uint32_t off = (row >= 0 && b < nqb) ? (uint32_t)((row * nqb + b) * 4) : kOutOfRange;
+      load_lds_b32(rsrc_s, off, __builtin_amdgcn_readfirstlane(scl_base + (uint32_t)p0 * 4));
+    }
+  }
 
   // LDS row of each of this wave's weight sub-tiles
   int nrow[TN];
@@ -351,37 +413,71 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 
 #define MOE_ISSUE_STAGE(buf, kt)                                                              \
   do {                                                                                        \
-    const uint32_t kb = (uint32_t)(kt) * ROWB;                                                \
     const uint32_t sb = smem_base + (uint32_t)(buf) * STAGE;                                  \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                           \
-        load_lds_b128(rsrc_a, aoff[j] + kb,                                                   \
+        load_lds_b128(rsrc_a, aoff[j] + (uint32_t)(kt) * ROWB,                                \
                       __builtin_amdgcn_readfirstlane(sb + (wave * LA + j) * 1024));           \
     _Pragma("unroll") for (int j = 0; j < LB; ++j)                                           \
-        load_lds_b128(rsrc_b, boff[j] + kb,                                                   \
+        load_lds_b128(rsrc_b, boff[j] + (uint32_t)(kt) * ROWW,                                \
                       __builtin_amdgcn_readfirstlane(sb + A_BYTES + (wave * LB + j) * 1024)); \
   } while (0)
 
-  // Fragment reads of sub-step kk of the stage in LDS buffer `buf`; the lane
-  // holds 8 consecutive k of its row: chunk 2*kk + lane/32 of the 128-byte row.
-#define MOE_LOAD_FRAGS(F, buf, kk)                                                             \
+  // Fragment reads of sub-step kk of stage kt (in LDS buffer `buf`); the
+  // lane holds 8 k values of its row. bf16 weights: chunk 2*kk + lane/32 of
+  // both 128-byte rows. fp8 weights: one 16-byte chunk of a 64-byte weight
+  // row holds 8 codes for each of two sub-steps, so sub-steps 2j and 2j+1
+  // take the two halves of chunk 2j + lane/32, and the token fragment reads
+  // the matching k values (a fixed permutation of k inside the stage, the
+  // same on both operands). Both chunks of a stage are read with its first
+  // sub-step; each sub-step's codes are widened, as bf16(fp32(code) * scale),
+  // after the matrix ops of the sub-step before it have been issued, so the
+  // conversion overlaps them.
+  uint32_t qraw[Q ? 2 : 1][Q ? TN : 1][4];
+  float qsc[Q ? TN : 1];
+#define MOE_LOAD_FRAGS(F, buf, kk, ktv)                                                        \
   do {                                                                                         \
     const char* sa_ = smem + (buf) * STAGE;                                                    \
     const char* sw_ = sa_ + A_BYTES;                                                           \
-    const int c_ = (kk) * 2 + (lane >> 5);                                                     \
+    const int h_ = lane >> 5;                                                                  \
+    const int c_ = Q ? 4 * ((kk) / 2) + 2 * h_ + ((kk) % 2) : (kk) * 2 + h_;                   \
     _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                        \
       const int r = wm * WTM + tm * 32 + (lane & 31);                                          \
       F##b[tm] = *reinterpret_cast<const bf16x8_t*>(sa_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
     }                                                                                          \
-    _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                        \
-      const int r = nrow[tn] + (lane & 31);                                                    \
-      F##a[tn] = *reinterpret_cast<const bf16x8_t*>(sw_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
+    if constexpr (!Q) {                                                                        \
+      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
+        const int r = nrow[tn] + (lane & 31);                                                  \
+        F##a[tn] = *reinterpret_cast<const bf16x8_t*>(sw_ + r * ROWW + ((c_ ^ swz<CPW>(r)) << 4)); \
+      }                                                                                        \
+    } else if ((kk) == 0) {                                                                    \
+      const int qb_ = (ktv) * BK / args.qblock;                                                \
+      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
+        const int r = nrow[tn] + (lane & 31);                                                  \
+        qsc[tn] = scl[r * sst + qb_];                                                          \
+        _Pragma("unroll") for (int pr = 0; pr < 2; ++pr) {                                     \
+          const u32x4_t v_ = *reinterpret_cast<const u32x4_t*>(                                \
+              sw_ + r * ROWW + (((2 * pr + h_) ^ swz<CPW>(r)) << 4));                          \
+          qraw[pr][tn][0] = v_[0];                                                             \
+          qraw[pr][tn][1] = v_[1];                                                             \
+          qraw[pr][tn][2] = v_[2];                                                             \
+          qraw[pr][tn][3] = v_[3];                                                             \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
+  // fp8 weights: widen the codes of sub-step kk into F##a
+#define MOE_WIDEN(F, kk)                                                                       \
+  do {                                                                                         \
+    if constexpr (Q) {                                                                         \
+      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                        \
+          F##a[tn] = fp8x8_to_bf16(qraw[(kk) / 2][tn][2 * ((kk) % 2)],                         \
+                                   qraw[(kk) / 2][tn][2 * ((kk) % 2) + 1], qsc[tn]);           \
     }                                                                                          \
   } while (0)
 
   constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
   static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
 
-  if constexpr (P == 0) {
   // prologue: stages 0..NS-1 in flight (one per buffer), stage 0 landed,
   // its first fragments read
 #pragma unroll
@@ -391,7 +487,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   else wait_vmcnt<0>();
   __syncthreads();
   bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-  MOE_LOAD_FRAGS(f0, 0, 0);
+  MOE_LOAD_FRAGS(f0, 0, 0, 0);
+  MOE_WIDEN(f0, 0);
 
   // Steady state. Fragments of the next sub-step are read before the matrix
   // ops of the current one. In the last sub-step of a stage its fragments
@@ -402,16 +499,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     const int buf = kt % NS;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      const bool more = kk + 1 < KK || kt + 1 < nk;
       if (kk + 1 < KK) {
-        if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, buf, kk + 1);
-        else MOE_LOAD_FRAGS(f0, buf, kk + 1);
+        if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, buf, kk + 1, kt);
+        else MOE_LOAD_FRAGS(f0, buf, kk + 1, kt);
       } else if (kt + 1 < nk) {
         // issued so far: stages 0 .. min(kt+NS-1, nk-1); stage kt+1 must have landed
         if (kt + NS - 1 < nk) wait_vmcnt<(NS - 2) * (LA + LB)>();
         else wait_vmcnt<0>();
         __syncthreads();  // stage kt+1 visible to all; every wave is done reading stage kt
         if (kt + NS < nk) MOE_ISSUE_STAGE(buf, kt + NS);
-        MOE_LOAD_FRAGS(f0, (kt + 1) % NS, 0);
+        MOE_LOAD_FRAGS(f0, (kt + 1) % NS, 0, kt + 1);
       }
       if (kk % 2 == 0) {
 #pragma unroll
@@ -419,105 +517,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #pragma unroll
           for (int tm = 0; tm < TM; ++tm)
             acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[tn], f0b[tm], acc[tn][tm], 0, 0, 0);
+        if (more) MOE_WIDEN(f1, (kk + 1) % KK);
       } else {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int tm = 0; tm < TM; ++tm)
             acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
+        if (more) MOE_WIDEN(f0, (kk + 1) % KK);
       }
     }
   }
-  } else {
-    // Register staging: stage s is loaded into register set s % P, P stages
-    // ahead of its use, and written to LDS buffer s % 2 one stage ahead. The
-    // VGPR file holds several times more bytes in flight than LDS could.
-    u32x4_t R[P][LA + LB];
-#define MOE_GLOAD(set, kt)                                                                     \
-  do {                                                                                         \
-    const uint32_t kb_ = (uint32_t)(kt) * ROWB;                                                \
-    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                            \
-        R[set][j] = __builtin_amdgcn_raw_buffer_load_b128(brsrc_a, aoff[j] + kb_, 0, 0);       \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                            \
-        R[set][LA + j] = __builtin_amdgcn_raw_buffer_load_b128(brsrc_b, boff[j] + kb_, 0, 0);  \
-  } while (0)
-#define MOE_SSTORE(set, buf)                                                                   \
-  do {                                                                                         \
-    char* sb_ = smem + (buf) * STAGE + lane * 16;                                              \
-    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                            \
-        *reinterpret_cast<u32x4_t*>(sb_ + (wave * LA + j) * 1024) = R[set][j];                 \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                            \
-        *reinterpret_cast<u32x4_t*>(sb_ + A_BYTES + (wave * LB + j) * 1024) = R[set][LA + j];  \
-  } while (0)
-#pragma unroll
-    for (int s2 = 0; s2 < P; ++s2)
-      if (s2 < nk) MOE_GLOAD(s2, s2);
-    MOE_SSTORE(0, 0);
-    if (P < nk) MOE_GLOAD(0, P);
-    __syncthreads();
-    bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-    MOE_LOAD_FRAGS(f0, 0, 0);
-    for (int kt0 = 0; kt0 < nk; kt0 += P) {
-#pragma unroll
-      for (int u = 0; u < P; ++u) {
-        const int kt = kt0 + u;
-        if (kt >= nk) break;
-        if (kt + 1 < nk) {
-          // buffer (kt+1)&1 was last read in stage kt-1, before its final barrier
-          MOE_SSTORE((u + 1) % P, (kt + 1) & 1);
-          if (kt + 1 + P < nk) MOE_GLOAD((u + 1) % P, kt + 1 + P);
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 1 < KK) {
-            if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, kt & 1, kk + 1);
-            else MOE_LOAD_FRAGS(f0, kt & 1, kk + 1);
-          } else if (kt + 1 < nk) {
-            __syncthreads();  // stage kt+1 written by all; stage kt read by all
-            MOE_LOAD_FRAGS(f0, (kt + 1) & 1, 0);
-          }
-          if (kk % 2 == 0) {
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-              for (int tm = 0; tm < TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[tn], f0b[tm], acc[tn][tm], 0, 0, 0);
-          } else {
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-              for (int tm = 0; tm < TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
-          }
-        }
-      }
-    }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
-  }
+#undef MOE_WIDEN
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
   tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane);
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int P, int MODE>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE, bool Q>
 hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const int64_t total = (int64_t)a.max_tiles * a.n_tiles;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-  grouped_gemm<BM, BN, BK, WGM, WGN, NS, P, MODE><<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0, stream>>>(a);
+  const size_t scl_bytes = Q ? ((size_t)BN * (a.nqb | 1) + 64) * sizeof(float) : 0;
+  grouped_gemm<BM, BN, BK, WGM, WGN, NS, MODE, Q>
+      <<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), scl_bytes, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool Q>
 hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   a.group_m = 8;
   // (token rows, weight rows, waves): the variants kept after sweeping tile
   // shape, pipeline depth and wave layout on the workloads' shapes
-  if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, 0, MODE>(a, stream);
-  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, 0, MODE>(a, stream);
-  if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, 0, MODE>(a, stream);
+  if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE, Q>(a, stream);
+  if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
+  if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -618,7 +654,7 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
   a.max_tiles = (int32_t)max_tiles;
   a.a_bytes = (uint32_t)(T * H * 2);
   a.n_tiles = (int)(I / (cfg.bn / 2));
-  return dispatch<kGateUpSilu>(cfg, a, stream);
+  return dispatch<kGateUpSilu, false>(cfg, a, stream);
 }
 
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
@@ -642,8 +678,73 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   a.topk = (int32_t)K;
   a.max_tiles = (int32_t)max_tiles;
   a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
-  if (out) return dispatch<kDownAtomic>(cfg, a, stream);
-  return dispatch<kDownSlot>(cfg, a, stream);
+  if (out) return dispatch<kDownAtomic, false>(cfg, a, stream);
+  return dispatch<kDownSlot, false>(cfg, a, stream);
+}
+
+bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block) {
+  return block % 64 == 0 && H / block <= kMaxScaleBlocks && I / block <= kMaxScaleBlocks;
+}
+
+hipError_t launch_gemm1_silu_fp8(GemmCfg cfg, const uint16_t* hidden, const uint8_t* w1q,
+                                 const float* w1s, int64_t block, const int32_t* sorted,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                 int64_t H, int64_t I, int64_t K, int64_t max_tiles,
+                                 uint16_t* act, const Epilogue& ep, hipStream_t stream) {
+  if (!fp8_gemm_supported(H, I, block)) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.act = ep.act;
+  a.alpha = ep.alpha;
+  a.limit = ep.limit;
+  a.bias = ep.b1;
+  a.a = hidden;
+  a.wq = w1q;
+  a.wscale = w1s;
+  a.qblock = (int32_t)block;
+  a.nqb = (int32_t)(H / block);
+  a.sorted = sorted;
+  a.tile_expert = tile_expert;
+  a.num_tiles = num_tiles;
+  a.out = act;
+  a.kdim = H;
+  a.n_out = I;
+  a.w_expert_stride = 2 * I * H;
+  a.inter = I;
+  a.topk = (int32_t)K;
+  a.max_tiles = (int32_t)max_tiles;
+  a.a_bytes = (uint32_t)(T * H * 2);
+  a.n_tiles = (int)(I / (cfg.bn / 2));
+  return dispatch<kGateUpSilu, true>(cfg, a, stream);
+}
+
+hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q,
+                            const float* w2s, int64_t block, const int32_t* sorted,
+                            const int32_t* tile_expert, const int32_t* num_tiles,
+                            const float* topk_weights, int64_t H, int64_t I, int64_t K,
+                            int64_t max_tiles, float* y, float* out, const float* b2,
+                            hipStream_t stream) {
+  if (!fp8_gemm_supported(H, I, block)) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.bias = out ? b2 : nullptr;  // on the slot path the combine adds b2
+  a.a = act;
+  a.wq = w2q;
+  a.wscale = w2s;
+  a.qblock = (int32_t)block;
+  a.nqb = (int32_t)(I / block);
+  a.sorted = sorted;
+  a.tile_expert = tile_expert;
+  a.num_tiles = num_tiles;
+  a.topk_weights = topk_weights;
+  a.out = out ? (void*)out : (void*)y;
+  a.kdim = I;
+  a.n_out = H;
+  a.w_expert_stride = H * I;
+  a.inter = I;
+  a.topk = (int32_t)K;
+  a.max_tiles = (int32_t)max_tiles;
+  a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
+  if (out) return dispatch<kDownAtomic, true>(cfg, a, stream);
+  return dispatch<kDownSlot, true>(cfg, a, stream);
 }
 
 }  // namespace moe

@@ -50,7 +50,6 @@ int hip_error(const char* what, hipError_t st) {
 constexpr double kSmallBatchUsPerWork = 1.4e-7;
 constexpr double kGroupedFixedUs = 60.0;
 constexpr double kGroupedUsPerWeightMB = 0.06;
-constexpr double kDequantBytesPerUs = 5.0e6;  // ~5 TB/s
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -82,6 +81,41 @@ int check_sizes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   return MOE_OK;
 }
 
+// FP8 weights on the grouped path: either the GEMMs read code tiles and
+// widen each fragment in registers, or one pass first widens every expert to
+// bf16 and the bf16 GEMMs run unchanged. In-register widening is repeated by
+// every row tile and wave that reads a weight tile: measured, it adds about
+// 0.45 us per GFLOP with 64- and 128-row tiles and 0.19 us per GFLOP with
+// 256-row tiles (more token rows per wave share each widened fragment). The
+// widening pass costs about 0.55 us per million weights, for all E experts.
+// So in-register widening wins with few rows per expert (many experts, few
+// tokens); the pass wins for dense experts.
+constexpr double kFp8InRegUsPerGflop128 = 0.45;
+constexpr double kFp8InRegUsPerGflop256 = 0.19;
+constexpr double kFp8WidenUsPerMWeight = 0.55;
+
+double fp8_widen_us(int64_t H, int64_t I, int64_t E) {
+  return kFp8WidenUsPerMWeight * 3.0 * (double)E * H * I * 1e-6;
+}
+
+double fp8_in_register_us(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
+  const int bm = moe::pick_gemm1_cfg(T, K, H, I, E).bm;
+  const double per_gflop = bm == 256 ? kFp8InRegUsPerGflop256 : kFp8InRegUsPerGflop128;
+  return per_gflop * 6.0 * (double)T * K * H * I * 1e-9;
+}
+
+// The grouped GEMMs can read FP8 tiles for every allowed block (a multiple
+// of 128) while the tile's scales fit in LDS.
+bool fp8_native_for_every_block(int64_t H, int64_t I) {
+  return moe::fp8_gemm_supported(H, I, 128);
+}
+
+// Whether the grouped path needs room for the widened weights.
+bool fp8_may_widen(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
+  return !fp8_native_for_every_block(H, I) ||
+         fp8_widen_us(H, I, E) <= fp8_in_register_us(T, H, I, E, K);
+}
+
 int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   // with FP8 weights the streaming paths move half the bytes and the
   // grouped path first widens every expert's weights to bf16
@@ -97,8 +131,12 @@ int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fl
   if (dec && slots <= std::max<int64_t>(K, E / 2)) return MOE_PATH_DECODE;
   const double routed_mb = (double)std::min<int64_t>(E, slots) * 6.0 * H * I / 1e6;
   const double sb_extra_us = kSmallBatchUsPerWork * (double)slots * H * I;
-  // widening all E experts: 1 byte read and 2 written per weight
-  const double dequant_us = fp8 ? (double)E * 3.0 * H * I * 3.0 / kDequantBytesPerUs : 0.0;
+  // what FP8 weights add to the grouped path (the cheaper way of widening)
+  const double dequant_us =
+      !fp8 ? 0.0
+           : fp8_native_for_every_block(H, I)
+                 ? std::min(fp8_widen_us(H, I, E), fp8_in_register_us(T, H, I, E, K))
+                 : fp8_widen_us(H, I, E);
   if (sb && sb_extra_us <= kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb + dequant_us)
     return MOE_PATH_SMALL_BATCH;
   return MOE_PATH_GROUPED;
@@ -114,7 +152,8 @@ struct Layout {
   bool decode = false;
   moe::GemmCfg g1{}, g2{};
   int64_t cap = 0, max_tiles = 0, nblk = 0;
-  size_t w1dq = 0, w2dq = 0;  // bf16 copies of FP8 weights (grouped path)
+  bool widened = false;       // room for bf16 copies of FP8 weights (grouped path)
+  size_t w1dq = 0, w2dq = 0;
   size_t err = 0, counts = 0, offsets = 0, num_tiles = 0, tile_expert = 0, sorted = 0,
          slot_of = 0, block_hist = 0, act = 0, y = 0, total = 0;
 };
@@ -156,7 +195,8 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.block_hist = take((size_t)E * L.nblk * 4);
   L.act = take((size_t)L.cap * I * 2);
   if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)n * H * 4);
-  if (flags & MOE_FLAG_FP8_WEIGHTS) {
+  if ((flags & MOE_FLAG_FP8_WEIGHTS) && fp8_may_widen(T, H, I, E, K)) {
+    L.widened = true;
     L.w1dq = take((size_t)E * 2 * I * H * 2);
     L.w2dq = take((size_t)E * H * I * 2);
   }
@@ -339,7 +379,11 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
     int32_t* block_hist = at<int32_t>(ws, L.block_hist);
     uint16_t* act = at<uint16_t>(ws, L.act);
     hipError_t st = hipSuccess;
-    if (q) {  // widen the FP8 weights to bf16 in the workspace
+    const bool q_native = q && moe::fp8_gemm_supported(H, I, q->block) &&
+                          fp8_in_register_us(T, H, I, E, K) < fp8_widen_us(H, I, E);
+    if (q && !q_native) {  // widen the FP8 weights to bf16 in the workspace
+      if (!L.widened)  // cannot happen: the layout plans for every block the check allows
+        return set_error(MOE_ERR_UNSUPPORTED, "no room for the widened FP8 weights");
       st = moe::launch_dequant_fp8(*q, E, H, I, at<uint16_t>(ws, L.w1dq),
                                    at<uint16_t>(ws, L.w2dq), stream);
       if ((rc = stage_check(flags, "dequant_fp8", st, stream)) != MOE_OK) return rc;
@@ -349,19 +393,30 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
     st = moe::launch_route(topk_ids, T, K, E, L.g1.bm, block_hist, counts, offsets,
                                       sorted, slot_of, tile_expert, num_tiles, stream);
     if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
-    st = moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I, K,
-                                L.max_tiles, act, ep, stream);
+    st = q_native ? moe::launch_gemm1_silu_fp8(L.g1, x, q->w1q, q->w1s, q->block, sorted,
+                                               tile_expert, num_tiles, T, H, I, K, L.max_tiles,
+                                               act, ep, stream)
+                  : moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I,
+                                           K, L.max_tiles, act, ep, stream);
     if ((rc = stage_check(flags, "gemm1_silu", st, stream)) != MOE_OK) return rc;
     if (flags & MOE_FLAG_ATOMIC_COMBINE) {
       st = moe::launch_zero(out, T * H, stream);
       if ((rc = stage_check(flags, "zero_out", st, stream)) != MOE_OK) return rc;
-      st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
-                             K, L.max_tiles, nullptr, out, ep.b2, stream);
+      st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
+                                            tile_expert, num_tiles, topk_weights, H, I, K,
+                                            L.max_tiles, nullptr, out, ep.b2, stream)
+                    : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
+                                        topk_weights, H, I, K, L.max_tiles, nullptr, out, ep.b2,
+                                        stream);
       if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
     } else {
       float* y = at<float>(ws, L.y);
-      st = moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles, topk_weights, H, I,
-                             K, L.max_tiles, y, nullptr, nullptr, stream);
+      st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
+                                            tile_expert, num_tiles, topk_weights, H, I, K,
+                                            L.max_tiles, y, nullptr, nullptr, stream)
+                    : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
+                                        topk_weights, H, I, K, L.max_tiles, y, nullptr, nullptr,
+                                        stream);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
       st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2, out,
                                stream);

@@ -50,6 +50,23 @@ struct GemmCfg {
 GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E);
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm);
 
+// FP8-weight grouped GEMMs: the weight tiles are staged as codes and widened
+// to bf16 (bf16_rne(fp32(code) * scale)) at fragment read; supported while
+// H/block and I/block are at most kMaxScaleBlocks (the tile's scales sit in LDS).
+constexpr int kMaxScaleBlocks = 32;
+bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block);
+hipError_t launch_gemm1_silu_fp8(GemmCfg cfg, const uint16_t* hidden, const uint8_t* w1q,
+                                 const float* w1s, int64_t block, const int32_t* sorted,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                 int64_t H, int64_t I, int64_t K, int64_t max_tiles,
+                                 uint16_t* act, const Epilogue& ep, hipStream_t stream);
+hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q,
+                            const float* w2s, int64_t block, const int32_t* sorted,
+                            const int32_t* tile_expert, const int32_t* num_tiles,
+                            const float* topk_weights, int64_t H, int64_t I, int64_t K,
+                            int64_t max_tiles, float* y, float* out, const float* b2,
+                            hipStream_t stream);
+
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,

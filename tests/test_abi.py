@@ -87,11 +87,18 @@ def test_fp8_argument_validation(lib):
     # null weights with T > 0
     assert lib.moe_forward_fp8(p, p, p, p, p, 128, p, p, 4, 512, 384, 8, 2, 0, f(1.702), f(7.0),
                                p, p, p, 0, p, 0, p) == moe.MOE_ERR_INVALID_ARG
-    # the grouped path's workspace holds the bf16 copy of the weights
+    # grouped path: with many experts and few rows each the GEMMs widen FP8
+    # fragments in registers (no extra workspace); for dense experts, or when
+    # H/128 or I/128 exceeds 32 (the tile's scales no longer fit in LDS), a
+    # pass first widens the weights into a bf16 copy in the workspace
     fl = moe.FLAG_FORCE_GROUPED
-    extra = (moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, fl | moe.FLAG_FP8_WEIGHTS)
-             - moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, fl))
-    assert extra >= 8 * 3 * 2048 * 2048 * 2
+
+    def extra(*shape):
+        return (moe.moe_workspace_bytes(*shape, fl | moe.FLAG_FP8_WEIGHTS)
+                - moe.moe_workspace_bytes(*shape, fl))
+    assert extra(8192, 4096, 384, 128, 8) == 0
+    assert extra(4195, 2048, 2048, 8, 2) >= 8 * 3 * 2048 * 2048 * 2
+    assert extra(100, 4224, 512, 8, 2) >= 8 * 3 * 4224 * 512 * 2
     assert moe.moe_path(1, 2048, 768, 128, 8, moe.FLAG_FP8_WEIGHTS) == moe.PATH_DECODE
 
 

@@ -112,6 +112,26 @@ def test_fp8_at_workload_size(name):
     _check(got[rows], want, tight, f"fp8/{name}")
 
 
+@pytest.mark.parametrize("H,I,block,native", [(4096, 256, 128, True),    # 32 scale blocks
+                                               (4224, 384, 128, False),   # 33: widened first
+                                               (4224, 256, 128, False)])
+def test_fp8_grouped_at_the_scale_block_limit(H, I, block, native):
+    """The grouped GEMMs keep a tile's scales in LDS for up to 32 blocks per
+    row; longer rows go through the bf16 widening pass. Both against the
+    oracle."""
+    require_gpu()
+    T, E, K = 150, 4, 2
+    d = cpu_inputs(T, H, I, E, K, seed=33)
+    q = make_fp8_weights(d, block)
+    dd, qd = to_device(d), _to_dev(q)
+    say(f"fp8 grouped H={H} I={I} block={block} native={native}")
+    got = _run(dd, qd, moe.FLAG_FORCE_GROUPED, {}, None)
+    rows = np.arange(T)
+    want = _oracle(d, q, rows, {"act": "silu"}, None)
+    tight = _oracle_widened(d, q, rows, {"act": "silu"}, None)
+    _check(got, want, tight, f"fp8/grouped H={H} I={I}")
+
+
 def test_fp8_caller_workspace_for_the_grouped_path():
     require_gpu()
     T, H, I, E, K = 200, 256, 256, 4, 2
