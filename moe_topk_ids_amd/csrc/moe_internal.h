@@ -13,7 +13,7 @@ namespace moe {
 // of routing workgroups stays at most kRouteMaxBlocks).
 constexpr int kRouteThreads = 256;
 // Problems up to this size are routed by one workgroup in one launch.
-constexpr int64_t kRouteSingleMaxSlots = 32768;
+constexpr int64_t kRouteSingleMaxSlots = 16384;
 constexpr int64_t kRouteSingleMaxExperts = 512;
 constexpr int kRouteMaxBlocks = 128;
 constexpr int kMaxExperts = 1024;

@@ -5,8 +5,8 @@
 //
 // Up to kRouteSingleMaxSlots slots (and kRouteSingleMaxExperts experts) one
 // workgroup of 16 waves does everything in a single launch (route_single):
-// the whole problem is a few hundred KB of ids, so the cost is the launch,
-// and a second launch plus a global histogram pass would double it.
+// every lane loads its (at most 32) ids at once, so the kernel pays one
+// memory latency, and ranking, counting and the scatter work from registers.
 //
 // Above that, two launches, no atomics on the ordering path:
 //   route_count    per workgroup, a per-expert histogram of its slot range
@@ -53,6 +53,7 @@ __device__ inline uint64_t lanemask_lt() {
 
 constexpr int kSingleThreads = 1024;
 constexpr int kSingleWaves = kSingleThreads / 64;
+constexpr int kSingleChunks = (int)(kRouteSingleMaxSlots / (kSingleWaves * 64));  // per lane
 
 __device__ inline void rank_and_scatter(const int32_t* __restrict__ ids, int64_t n_slots,
                                         int32_t E, int64_t wbase, int64_t per_wave,
@@ -190,60 +191,91 @@ __global__ __launch_bounds__(kSingleThreads) void route_single(
   int32_t* run = lds;
   int32_t* tot = run + kSingleWaves * E;
   int32_t* off = tot + E;
-  __shared__ int32_t part[kSingleThreads];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
 
+  // every id of the wave's contiguous, 64-aligned slot range is loaded up
+  // front (one memory latency for the whole kernel)
+  const int64_t per_wave = ((n_slots + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
+  const int64_t wbase = (int64_t)wave * per_wave;
+  int32_t idr[kSingleChunks];
+#pragma unroll
+  for (int c = 0; c < kSingleChunks; ++c) {
+    const int64_t f = wbase + c * 64 + lane;
+    idr[c] = (c * 64 < per_wave && f < n_slots) ? ids[f] : -1;
+  }
   for (int i = tid; i < kSingleWaves * E; i += kSingleThreads) run[i] = 0;
   __syncthreads();
 
-  // 1. per-wave counts over contiguous, 64-aligned slot ranges
-  const int64_t per_wave = ((n_slots + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
-  const int64_t wbase = (int64_t)wave * per_wave;
+  // 1. rank each chunk by ballot (lowest lane first among equal ids); the
+  //    group's first lane bumps the wave's count of that expert, and the
+  //    value it read is the group's start inside the wave
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
   int32_t* myrun = run + wave * E;
-  for (int64_t i = lane; i < per_wave; i += 64) {
-    const int64_t f = wbase + i;
-    if (f >= n_slots) break;
-    const int32_t e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&myrun[e], 1);
-  }
-  __syncthreads();
-
-  // 2. per expert: total, and each wave's exclusive prefix inside the expert
-  for (int e = tid; e < E; e += kSingleThreads) {
-    int32_t a = 0;
-    for (int w = 0; w < kSingleWaves; ++w) {
-      const int32_t c = run[w * E + e];
-      run[w * E + e] = a;
-      a += c;
+#pragma unroll
+  for (int c = 0; c < kSingleChunks; ++c) {
+    if (c * 64 >= per_wave) break;  // uniform
+    const int32_t e = idr[c];
+    const bool valid = e >= 0 && e < E;
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t bm = __ballot(set);
+      mask &= set ? bm : ~bm;
     }
-    tot[e] = a;
+    const int32_t rank = __popcll(mask & lanemask_lt());
+    int32_t start = 0;
+    if (valid && rank == 0) start = atomicAdd(&myrun[e], __popcll(mask));
+    const int leader = valid ? __ffsll((long long)mask) - 1 : lane;
+    start = __shfl(start, leader, 64);
+    // keep (place in the wave, expert) in the id's register: place < 2048,
+    // expert < 512
+    idr[c] = valid ? ((start + rank) << 11) | e : -1;
   }
   __syncthreads();
 
-  // 3. exclusive scan over experts of the padded counts
-  const int per = (E + kSingleThreads - 1) / kSingleThreads;
-  const int e0 = tid * per;
-  int32_t local = 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) local += (tot[e] + M - 1) / M * M;
-  part[tid] = local;
-  __syncthreads();
-  for (int d = 1; d < kSingleThreads; d <<= 1) {
-    const int32_t v = tid >= d ? part[tid - d] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // 2. and 3. in wave 0: per expert the total and each wave's exclusive
+  //    prefix inside the expert (the 16 per-wave counts read together), then
+  //    an exclusive scan of the padded counts over experts with shuffles;
+  //    lane l owns experts l*EPL .. l*EPL+EPL-1
+  if (wave == 0) {
+    const int epl = (E + 63) / 64;
+    int32_t lane_sum = 0;
+    for (int q = 0; q < epl; ++q) {
+      const int e = lane * epl + q;
+      if (e >= E) break;
+      int32_t cw[kSingleWaves];
+#pragma unroll
+      for (int w = 0; w < kSingleWaves; ++w) cw[w] = run[w * E + e];
+      int32_t a = 0;
+#pragma unroll
+      for (int w = 0; w < kSingleWaves; ++w) {
+        run[w * E + e] = a;
+        a += cw[w];
+      }
+      tot[e] = a;
+      lane_sum += (a + M - 1) / M * M;
+    }
+    int32_t incl = lane_sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    int32_t acc = incl - lane_sum;
+    for (int q = 0; q < epl; ++q) {
+      const int e = lane * epl + q;
+      if (e >= E) break;
+      off[e] = acc;
+      acc += (tot[e] + M - 1) / M * M;
+    }
+    if (lane == 63) off[E] = incl;
   }
-  int32_t acc = part[tid] - local;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    off[e] = acc;
-    acc += (tot[e] + M - 1) / M * M;
-  }
-  if (tid == kSingleThreads - 1) off[E] = part[tid];
   __syncthreads();
 
-  // 4. metadata, pad rows, tile->expert map; waves' absolute first rows
+  // 4. metadata, pad rows, tile->expert map
   for (int e = tid; e < E; e += kSingleThreads) counts[e] = tot[e];
   for (int e = tid; e <= E; e += kSingleThreads) offsets[e] = off[e];
   if (tid == 0) num_tiles[0] = off[E] / M;
@@ -252,11 +284,23 @@ __global__ __launch_bounds__(kSingleThreads) void route_single(
     for (int32_t j = lane; j < padded / M; j += 64) tile_expert[start / M + j] = (int32_t)e;
     for (int32_t r = tot[e] + lane; r < padded; r += 64) sorted[start + r] = -1;
   }
-  for (int i = tid; i < kSingleWaves * E; i += kSingleThreads) run[i] += off[i % E];
-  __syncthreads();
 
-  // 5. stable scatter
-  rank_and_scatter(ids, n_slots, E, wbase, per_wave, myrun, sorted, slot_of);
+  // 5. scatter: row = expert start + earlier waves' count + place in the wave
+#pragma unroll
+  for (int c = 0; c < kSingleChunks; ++c) {
+    if (c * 64 >= per_wave) break;  // uniform
+    const int64_t f = wbase + c * 64 + lane;
+    const bool in = f < n_slots;
+    const int32_t v = idr[c];
+    if (in && v >= 0) {
+      const int32_t e = v & 0x7ff;
+      const int32_t pos = off[e] + run[wave * E + e] + (v >> 11);
+      sorted[pos] = (int32_t)f;
+      slot_of[f] = pos;
+    } else if (in) {
+      slot_of[f] = -1;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void validate_ids(const int32_t* __restrict__ ids,

@@ -72,10 +72,10 @@ def test_route_edge_cases(case):
         ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = -3
         ids[rng.integers(0, 300, 20), rng.integers(0, 4, 20)] = 16
         _check_route(ids, 16, 64, case)
-    elif case == "single_wg_limit":  # 32768 slots, 512 experts: the one-workgroup form's limit
-        _check_route(_rand_ids(4096, 8, 512, 12), 512, 64, case)
-    elif case == "multi_wg_just_past":  # 32776 slots: the two-launch form
-        _check_route(_rand_ids(4097, 8, 64, 13), 64, 128, case)
+    elif case == "single_wg_limit":  # 16384 slots, 512 experts: the one-workgroup form's limit
+        _check_route(_rand_ids(2048, 8, 512, 12), 512, 64, case)
+    elif case == "multi_wg_just_past":  # 16392 slots: the two-launch form
+        _check_route(_rand_ids(2049, 8, 64, 13), 64, 128, case)
     elif case == "multi_wg_out_of_range":
         ids = _rand_ids(5000, 8, 64, 14)
         ids[rng.integers(0, 5000, 200), rng.integers(0, 8, 200)] = -1
