@@ -382,20 +382,32 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS,
                 "algorithmic_bytes": alg_bytes, "avg_launch_us": dur_ms * 1e3}
     else:
-        if fp8:  # the grouped path runs its GEMMs on the bf16-widened weights
-            w1s = [dev["w1"]]
-            copies = 1
-        kernel = "grouped_gemm_gate_up_silu"
         M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
         r = moe.moe_route(dev["topk_ids"], s.E, M)
         act = torch.empty((r["capacity"], s.I), dtype=torch.bfloat16, device="cuda")
+        if fp8 and moe.moe_fp8_widens_in_gemm(s.T, s.H, s.I, s.E, s.K, block):
+            # the forward's GEMM1 reads the FP8 codes and widens them in registers
+            kernel = "grouped_gemm_gate_up_silu_fp8"
+
+            def gemm1(i):
+                c = qs[i % copies]
+                moe.moe_gemm1_silu_fp8(dev["hidden_states"], c["w1q"], c["w1s"], block, r, s.K,
+                                       M, act=act)
+        else:
+            if fp8:  # the forward widens the weights first; its GEMM1 is the bf16 one
+                w1s = [dev["w1"]]
+                copies = 1
+            kernel = "grouped_gemm_gate_up_silu"
+
+            def gemm1(i):
+                moe.moe_gemm1_silu(dev["hidden_states"], w1s[i % copies], r, s.K, M, act=act)
         for i in range(3):
-            moe.moe_gemm1_silu(dev["hidden_states"], w1s[i % copies], r, s.K, M, act=act)
+            gemm1(i)
         reps = max(args.steps, 20)
         torch.cuda.synchronize()
         ev0.record(stream)
         for i in range(reps):
-            moe.moe_gemm1_silu(dev["hidden_states"], w1s[i % copies], r, s.K, M, act=act)
+            gemm1(i)
         ev1.record(stream)
         torch.cuda.synchronize()
         dur_ms = ev0.elapsed_time(ev1) / reps

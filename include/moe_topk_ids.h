@@ -227,6 +227,27 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    int64_t max_tiles, void* act, void* stream);
 
 /*
+ * moe_gemm1_silu with FP8 E4M3 gate/up weights (the layout of
+ * moe_forward_fp8: w1q uint8 [E, 2I, H], w1_scale fp32 [E, 2I, H/block]):
+ * the weight tiles are read as codes and each fragment is widened in
+ * registers to bf16_rne(fp32(code) * scale) before the bf16 matrix ops, the
+ * step tpu-inference's fused_moe kernel.py (sub-channel quantisation)
+ * performs when it scales each contraction block of its w1/w3 product.
+ * Also MOE_ERR_UNSUPPORTED when H/block or I/block exceeds 32.
+ */
+int moe_gemm1_silu_fp8(const void* hidden, const uint8_t* w1q, const float* w1_scale,
+                       int64_t block, const int32_t* sorted, const int32_t* tile_expert,
+                       const int32_t* num_tiles, int64_t T, int64_t H, int64_t I, int64_t E,
+                       int64_t K, int32_t m_tile, int64_t max_tiles, void* act, void* stream);
+
+/* With FP8 weights the grouped path either widens fragments inside its GEMMs
+ * (returns 1) or first widens every expert to bf16 in the workspace and runs
+ * the bf16 GEMMs (returns 0), whichever is cheaper for these sizes; negative
+ * MOE_ERR_* on invalid sizes or block. */
+int moe_fp8_widens_in_gemm(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                           int64_t block);
+
+/*
  * The router that produces topk_weights / topk_ids from fp32 router logits
  * [T,E] (the softmax-then-top-k step of the atrex-bench #009 "Input
  * Generation" section, tpu-inference get_top_k, metrale

@@ -87,6 +87,11 @@ def load_library():
     lib.moe_route_scratch_bytes.restype = sz
     lib.moe_gemm1_silu.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, i64, p, p]
     lib.moe_gemm1_silu.restype = ctypes.c_int
+    lib.moe_gemm1_silu_fp8.argtypes = [p, p, p, i64, p, p, p, i64, i64, i64, i64, i64, i32, i64,
+                                       p, p]
+    lib.moe_gemm1_silu_fp8.restype = ctypes.c_int
+    lib.moe_fp8_widens_in_gemm.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.moe_fp8_widens_in_gemm.restype = ctypes.c_int
     lib.moe_topk_softmax.argtypes = [p, i64, i64, i64, ctypes.c_int, p, p, p]
     lib.moe_topk_softmax.restype = ctypes.c_int
     lib.moe_last_error.argtypes = []
@@ -322,6 +327,44 @@ def moe_gemm1_silu(hidden_states, w1, route: dict, K: int, m_tile: int, act=None
                               _ptr(route["tile_expert"]), _ptr(route["num_tiles"]), T, H, I, E, K,
                               m_tile, cap // m_tile, _ptr(act), _stream(stream)))
     return act
+
+
+def moe_gemm1_silu_fp8(hidden_states, w1q, w1_scale, block: int, route: dict, K: int,
+                       m_tile: int, act=None, stream=None):
+    """moe_gemm1_silu with FP8 E4M3 gate/up weights (uint8 codes [E,2I,H],
+    fp32 scales [E,2I,H/block]) widened in registers."""
+    import torch
+
+    lib = load_library()
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(w1q, "w1q", torch.uint8, 3)
+    _need(w1_scale, "w1_scale", torch.float32, 3)
+    T, H = hidden_states.shape
+    E, I2, _ = w1q.shape
+    I = I2 // 2
+    if tuple(w1q.shape) != (E, 2 * I, H) or tuple(w1_scale.shape) != (E, 2 * I, H // block):
+        raise ValueError("w1q must be [E,2I,H] and w1_scale [E,2I,H/block]")
+    cap = route["capacity"]
+    if act is None:
+        act = torch.zeros((max(cap, 1), I), dtype=torch.bfloat16, device=hidden_states.device)
+    else:
+        _need(act, "act", torch.bfloat16, 2)
+        if act.shape[0] < cap or act.shape[1] != I:
+            raise ValueError("act must be at least [capacity, I]")
+    _check(lib.moe_gemm1_silu_fp8(_ptr(hidden_states), _ptr(w1q), _ptr(w1_scale), block,
+                                  _ptr(route["sorted"]), _ptr(route["tile_expert"]),
+                                  _ptr(route["num_tiles"]), T, H, I, E, K, m_tile, cap // m_tile,
+                                  _ptr(act), _stream(stream)))
+    return act
+
+
+def moe_fp8_widens_in_gemm(T: int, H: int, I: int, E: int, K: int, block: int) -> bool:
+    """True when the grouped path widens FP8 fragments inside its GEMMs, False
+    when it first widens the weights to bf16 in the workspace."""
+    rc = load_library().moe_fp8_widens_in_gemm(T, H, I, E, K, block)
+    if rc < 0:
+        _check(rc)
+    return rc == 1
 
 
 def moe_topk_softmax(router_logits, top_k: int, renormalize: bool = True, topk_weights=None,

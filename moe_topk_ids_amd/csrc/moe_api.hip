@@ -110,6 +110,13 @@ bool fp8_native_for_every_block(int64_t H, int64_t I) {
   return moe::fp8_gemm_supported(H, I, 128);
 }
 
+// Whether the grouped path widens FP8 fragments inside its GEMMs (else it
+// runs the widening pass first).
+bool fp8_grouped_in_gemm(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int64_t block) {
+  return moe::fp8_gemm_supported(H, I, block) &&
+         fp8_in_register_us(T, H, I, E, K) < fp8_widen_us(H, I, E);
+}
+
 // Whether the grouped path needs room for the widened weights.
 bool fp8_may_widen(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   return !fp8_native_for_every_block(H, I) ||
@@ -379,8 +386,7 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
     int32_t* block_hist = at<int32_t>(ws, L.block_hist);
     uint16_t* act = at<uint16_t>(ws, L.act);
     hipError_t st = hipSuccess;
-    const bool q_native = q && moe::fp8_gemm_supported(H, I, q->block) &&
-                          fp8_in_register_us(T, H, I, E, K) < fp8_widen_us(H, I, E);
+    const bool q_native = q && fp8_grouped_in_gemm(T, H, I, E, K, q->block);
     if (q && !q_native) {  // widen the FP8 weights to bf16 in the workspace
       if (!L.widened)  // cannot happen: the layout plans for every block the check allows
         return set_error(MOE_ERR_UNSUPPORTED, "no room for the widened FP8 weights");
@@ -542,6 +548,40 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
       static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
       static_cast<uint16_t*>(act), moe::Epilogue{}, static_cast<hipStream_t>(stream));
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
+}
+
+int moe_gemm1_silu_fp8(const void* hidden, const uint8_t* w1q, const float* w1_scale,
+                       int64_t block, const int32_t* sorted, const int32_t* tile_expert,
+                       const int32_t* num_tiles, int64_t T, int64_t H, int64_t I, int64_t E,
+                       int64_t K, int32_t m_tile, int64_t max_tiles, void* act, void* stream) {
+  int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (m_tile != 64 && m_tile != 128 && m_tile != 256)
+    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128 and 256", m_tile);
+  if (!moe::fp8_block_ok(H, I, block) || !moe::fp8_gemm_supported(H, I, block))
+    return set_error(MOE_ERR_UNSUPPORTED,
+                     "scale block %lld: needs a multiple of 128 dividing H=%lld and I=%lld, "
+                     "with at most %d blocks per row",
+                     (long long)block, (long long)H, (long long)I, moe::kMaxScaleBlocks);
+  if (max_tiles < 0 || max_tiles > INT32_MAX)
+    return set_error(MOE_ERR_INVALID_ARG, "max_tiles=%lld", (long long)max_tiles);
+  if (T == 0 || max_tiles == 0) return MOE_OK;
+  if (!hidden || !w1q || !w1_scale || !sorted || !tile_expert || !num_tiles || !act)
+    return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
+  hipError_t st = moe::launch_gemm1_silu_fp8(
+      moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256}, static_cast<const uint16_t*>(hidden), w1q,
+      w1_scale, block, sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
+      static_cast<uint16_t*>(act), moe::Epilogue{}, static_cast<hipStream_t>(stream));
+  return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu_fp8", st);
+}
+
+int moe_fp8_widens_in_gemm(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                           int64_t block) {
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (!moe::fp8_block_ok(H, I, block))
+    return set_error(MOE_ERR_UNSUPPORTED, "scale block %lld", (long long)block);
+  return fp8_grouped_in_gemm(T, H, I, E, K, block) ? 1 : 0;
 }
 
 int moe_topk_softmax(const float* router_logits, int64_t T, int64_t E, int64_t K,

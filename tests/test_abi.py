@@ -30,7 +30,8 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
-              "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act", "moe_forward_fp8"):
+              "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act", "moe_forward_fp8",
+              "moe_gemm1_silu_fp8", "moe_fp8_widens_in_gemm"):
         assert n in names
 
 
@@ -100,6 +101,15 @@ def test_fp8_argument_validation(lib):
     assert extra(4195, 2048, 2048, 8, 2) >= 8 * 3 * 2048 * 2048 * 2
     assert extra(100, 4224, 512, 8, 2) >= 8 * 3 * 4224 * 512 * 2
     assert moe.moe_path(1, 2048, 768, 128, 8, moe.FLAG_FP8_WEIGHTS) == moe.PATH_DECODE
+    # which widening the grouped path takes
+    assert moe.moe_fp8_widens_in_gemm(8192, 4096, 384, 128, 8, 128)      # many experts, few rows
+    assert not moe.moe_fp8_widens_in_gemm(4195, 2048, 2048, 8, 2, 256)  # dense experts
+    assert not moe.moe_fp8_widens_in_gemm(100, 4224, 512, 8, 2, 128)    # 33 scale blocks per row
+    assert lib.moe_fp8_widens_in_gemm(4, 512, 384, 8, 2, 200) == moe.MOE_ERR_UNSUPPORTED
+    # the standalone FP8 GEMM1 checks its block before touching a device
+    for block, H in ((64, 512), (128, 4224)):
+        rc = lib.moe_gemm1_silu_fp8(p, p, p, block, p, p, p, 4, H, 384, 8, 2, 128, 1, p, p)
+        assert rc == moe.MOE_ERR_UNSUPPORTED, (block, H)
 
 
 def test_route_argument_validation(lib):

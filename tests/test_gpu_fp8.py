@@ -132,6 +132,37 @@ def test_fp8_grouped_at_the_scale_block_limit(H, I, block, native):
     _check(got, want, tight, f"fp8/grouped H={H} I={I}")
 
 
+@pytest.mark.parametrize("name", ["tiny", "wide"])
+def test_fp8_gemm1_intermediate(name):
+    """moe_gemm1_silu_fp8 (codes widened in registers) vs the oracle's per-slot
+    bf16 activation on the bf16-widened weights: at most one bf16 ulp apart
+    (the k order inside a stage differs), nearly all identical."""
+    require_gpu()
+    s = SHAPES[name]
+    d = shape_inputs(name)
+    q = make_fp8_weights(d, 128)
+    dd, qd = to_device(d), _to_dev(q)
+    M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
+    say(f"fp8 intermediate {name} M={M}")
+    r = moe.moe_route(dd["topk_ids"], s.E, M)
+    act = moe.moe_gemm1_silu_fp8(dd["hidden_states"], qd["w1q"], qd["w1s"], 128, r, s.K, M)
+    torch.cuda.synchronize()
+    slot_of = r["slot_of"].cpu().numpy()
+    rows = sample_rows(s.T, 48, seed=4)
+    slots = (rows[:, None] * s.K + np.arange(s.K)[None, :]).ravel()
+    got = act.cpu().view(torch.int16).numpy().view(np.uint16)[slot_of[slots]]
+    w1, _ = _widened(q, 128)
+    want = oracle.slot_act_bf16(bf16_bits(d["hidden_states"])[rows], bf16_bits(w1),
+                                d["topk_ids"].numpy()[rows])
+    gf = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+    wf = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
+    tol = 2.0 ** -7 * np.maximum(np.abs(gf), np.abs(wf)) + 1e-7
+    exact = float(np.mean(got == want))
+    say(f"  identical {exact:.4f}, max |diff| {np.max(np.abs(gf - wf)):.3e}")
+    assert np.all(np.abs(gf - wf) <= tol)
+    assert exact >= 0.97
+
+
 def test_fp8_caller_workspace_for_the_grouped_path():
     require_gpu()
     T, H, I, E, K = 200, 256, 256, 4, 2
