@@ -17,37 +17,80 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-
+// A workgroup loops over tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...;
+// its lanes cover NC float4 columns each of the row's blockIdx.y-th block of
+// 256 * NC columns. Per token, the slot lookups and weights are wave-uniform
+// (scalar loads), and each lane issues the loads of KP slot rows x NC
+// columns before the first use, then adds them in k order. A dropped slot is
+// skipped by a select, never by a branch around its load (its row is loaded
+// from a valid address and discarded).
+template <int KP, int NC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float* __restrict__ y, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ ids, int32_t E, int64_t T,
     int64_t H, int32_t K, const float* __restrict__ b2, float* __restrict__ out) {
 #pragma clang fp contract(off)
   const int64_t h4 = H / 4;
-  const int64_t n = T * h4;
-  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < n;
-       q += (int64_t)gridDim.x * kThreads) {
-    const int64_t t = q / h4;
-    const int64_t c = q - t * h4;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const int64_t f = t * K + k;
-      if (slot_of ? slot_of[f] < 0 : (uint32_t)ids[f] >= (uint32_t)E) continue;
-      const float w = topk_weights[f];
-      float4 v = reinterpret_cast<const float4*>(y + f * H)[c];
-      if (b2) {  // w * (y + b2[e]): the expert's bias before its routing weight
-        const float4 b = reinterpret_cast<const float4*>(b2 + (int64_t)ids[f] * H)[c];
-        v.x = v.x + b.x;
-        v.y = v.y + b.y;
-        v.z = v.z + b.z;
-        v.w = v.w + b.w;
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  const float4* b4 = reinterpret_cast<const float4*>(b2);
+  const int64_t c0 = (int64_t)blockIdx.y * kThreads * NC + threadIdx.x;
+  int64_t col[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = c0 + (int64_t)kThreads * i;
+    col[i] = c < h4 ? c : h4 - 1;  // lanes past the row end load a valid column
+  }
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    float4 o[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < K; k0 += KP) {
+      float4 v[KP][NC];
+      float w[KP];
+      bool live[KP];
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const int k = k0 + j < K ? k0 + j : K - 1;
+        const int64_t f = t * K + k;
+        const int32_t e = ids[f];
+        const bool in = (uint32_t)e < (uint32_t)E;
+        live[j] = k0 + j < K && (slot_of ? slot_of[f] >= 0 : in);
+        w[j] = topk_weights[f];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) v[j][i] = y4[f * h4 + col[i]];
+        if (b2) {  // w * (y + b2[e]): the expert's bias before its routing weight
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const float4 b = b4[(in ? (int64_t)e : 0) * h4 + col[i]];
+            v[j][i].x = v[j][i].x + b.x;
+            v[j][i].y = v[j][i].y + b.y;
+            v[j][i].z = v[j][i].z + b.z;
+            v[j][i].w = v[j][i].w + b.w;
+          }
+        }
       }
-      o.x = o.x + w * v.x;
-      o.y = o.y + w * v.y;
-      o.z = o.z + w * v.z;
-      o.w = o.w + w * v.w;
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          // component-wise selects (a select of the whole vector would
+          // go through private memory)
+          const float nx = o[i].x + w[j] * v[j][i].x;
+          const float ny = o[i].y + w[j] * v[j][i].y;
+          const float nz = o[i].z + w[j] * v[j][i].z;
+          const float nw = o[i].w + w[j] * v[j][i].w;
+          o[i].x = live[j] ? nx : o[i].x;
+          o[i].y = live[j] ? ny : o[i].y;
+          o[i].z = live[j] ? nz : o[i].z;
+          o[i].w = live[j] ? nw : o[i].w;
+        }
+      }
     }
-    reinterpret_cast<float4*>(out + t * H)[c] = o;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = c0 + (int64_t)kThreads * i;
+      if (c < h4) reinterpret_cast<float4*>(out + t * H)[c] = o[i];
+    }
   }
 }
 
@@ -70,8 +113,25 @@ hipError_t launch_combine(const float* y, const float* topk_weights, const int32
                           const float* b2, float* out, hipStream_t stream) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
-  combine_kernel<<<grid_for(n), kThreads, 0, stream>>>(y, topk_weights, slot_of, topk_ids,
-                                                         (int32_t)E, T, H, (int32_t)K, b2, out);
+  const int64_t nc = (H / 4 + kThreads - 1) / kThreads;  // float4 columns per lane
+  // rows wider than 8192 floats: column blocks of 8192 along grid.y
+  const dim3 grid((unsigned)(T < 2048 ? T : 2048), (unsigned)((nc + 7) / 8));
+#define MOE_COMBINE(KP, NC)                                                                    \
+  combine_kernel<KP, NC><<<grid, kThreads, 0, stream>>>(y, topk_weights, slot_of, topk_ids,    \
+                                                        (int32_t)E, T, H, (int32_t)K, b2, out)
+#define MOE_COMBINE_NC(KP)            \
+  do {                                \
+    if (nc <= 1) MOE_COMBINE(KP, 1);  \
+    else if (nc <= 2) MOE_COMBINE(KP, 2); \
+    else if (nc <= 4) MOE_COMBINE(KP, 4); \
+    else MOE_COMBINE(KP, 8);          \
+  } while (0)
+  if (K <= 1) MOE_COMBINE_NC(1);
+  else if (K <= 2) MOE_COMBINE_NC(2);
+  else if (K <= 4 || nc > 4) MOE_COMBINE_NC(4);  // at most 16 float4 loads in flight per lane
+  else MOE_COMBINE_NC(8);
+#undef MOE_COMBINE_NC
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

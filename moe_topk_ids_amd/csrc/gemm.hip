@@ -66,6 +66,7 @@ struct GemmArgs {
   int32_t max_tiles;        // row tiles the grid was sized for
   int32_t n_tiles;          // weight-row tiles
   int32_t group_m;          // row tiles per scheduling group
+  int32_t xcd_slots;        // workgroups resident at once on one XCD
   // epilogue variants: activation kind and swigluoai parameters (GEMM1),
   // bias b1 [E, 2I] (GEMM1) or b2 [E, H] (GEMM2 with the atomic combine)
   int32_t act;
@@ -301,14 +302,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int wm = wave % WGM;
   const int wn = wave / WGM;
 
-  // XCD-aware tile order: consecutive workgroup ids are dealt round-robin to
-  // the 8 XCDs, so hand each XCD a contiguous run of logical tiles; inside
-  // it, groups of GM row tiles sweep the weight tiles so that the tiles
-  // resident on one XCD share token rows and weight rows in its L2.
+  // XCD-aware tile order. Logical tiles are ordered in groups of GM row
+  // tiles that sweep the weight tiles. Consecutive workgroup ids are dealt
+  // round-robin to the 8 XCDs, so the workgroup in slot s of XCD x takes
+  // tile w*8S + x*S + s%S of window w = s/S, S being the workgroups one XCD
+  // holds at once: the XCDs work through the same window of 8S tiles
+  // together (one expert's weights and token rows, which the last-level
+  // cache then serves to all of them), each on a contiguous run of S tiles
+  // that share rows in its own L2. The last, partial window is shared out
+  // evenly over the XCDs.
   const int n_tiles = args.n_tiles;
   const int total = args.max_tiles * n_tiles;
-  const int per_xcd = gridDim.x / 8;
-  const int pid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int S = args.xcd_slots;
+  const int slot = blockIdx.x / 8;
+  const int nfull = total / (8 * S);
+  const int pid = slot < nfull * S
+                      ? (slot / S) * 8 * S + (blockIdx.x % 8) * S + slot % S
+                      : nfull * 8 * S + (blockIdx.x % 8) * ((total - nfull * 8 * S + 7) / 8) +
+                            (slot - nfull * S);
   if (pid >= total) return;
   const int group = pid / (args.group_m * n_tiles);
   const int first_m = group * args.group_m;
@@ -539,8 +550,13 @@ template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE, bool Q>
 hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const int64_t total = (int64_t)a.max_tiles * a.n_tiles;
   if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 7) / 8 * 8;  // whole rounds over the 8 XCDs
   const size_t scl_bytes = Q ? ((size_t)BN * (a.nqb | 1) + 64) * sizeof(float) : 0;
+  // workgroups one CU holds at once (LDS-bound: 160 KB per CU), 32 CUs per XCD
+  constexpr size_t kStageBytes = (size_t)BM * BK * 2 + (size_t)BN * BK * (Q ? 1 : 2);
+  const int64_t per_cu = (int64_t)((160 * 1024) / (NS * kStageBytes + scl_bytes));
+  a.xcd_slots = (int32_t)(32 * (per_cu < 1 ? 1 : per_cu));
+  const int64_t S = a.xcd_slots, nfull = total / (8 * S);
+  const int64_t blocks = 8 * (nfull * S + (total - nfull * 8 * S + 7) / 8);
   grouped_gemm<BM, BN, BK, WGM, WGN, NS, MODE, Q>
       <<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), scl_bytes, stream>>>(a);
   return hipGetLastError();
