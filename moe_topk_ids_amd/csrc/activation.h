@@ -27,6 +27,13 @@ struct Epilogue {
   bool plain() const { return act == kActSilu && b1 == nullptr && b2 == nullptr; }
 };
 
+// silu(g) * u = g * u / (1 + exp(-g)), exp via the hardware 2^x: the plain
+// epilogue of the gate/up projection.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // act(g, u) for the variants (silu included). tanh(z) = 1 - 2 / (e^{2z} + 1)
 // and the sigmoid use the hardware exp and reciprocal; the error is far
 // inside the bf16 rounding of the stored activation.

@@ -10,7 +10,9 @@
 // kernel.py. Products and sums are rounded separately (contraction into
 // fused multiply-adds is switched off), in the oracle's order; as the
 // hardware fp32 atomic add rounds to nearest even too, for K <= 2 this gives
-// the same bits as the atomic path's 0 + a + b in either order.
+// the same bits as the atomic path's 0 + a + b in either order (when the
+// down projection's contraction is not split: the atomic path never splits
+// it, and its partial rows would be summed before the weight here).
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,9 +30,11 @@ template <int KP, int NC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float* __restrict__ y, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ ids, int32_t E, int64_t T,
-    int64_t H, int32_t K, const float* __restrict__ b2, float* __restrict__ out) {
+    int64_t H, int32_t K, const float* __restrict__ b2, float* __restrict__ out,
+    int32_t ksplit) {
 #pragma clang fp contract(off)
   const int64_t h4 = H / 4;
+  const int64_t split4 = T * K * h4;  // float4s per partial slot buffer
   const float4* y4 = reinterpret_cast<const float4*>(y);
   const float4* b4 = reinterpret_cast<const float4*>(b2);
   const int64_t c0 = (int64_t)blockIdx.y * kThreads * NC + threadIdx.x;
@@ -58,6 +62,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         w[j] = topk_weights[f];
 #pragma unroll
         for (int i = 0; i < NC; ++i) v[j][i] = y4[f * h4 + col[i]];
+        for (int s = 1; s < ksplit; ++s) {  // partial sums of a split contraction, in order
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const float4 p = y4[s * split4 + f * h4 + col[i]];
+            v[j][i].x = v[j][i].x + p.x;
+            v[j][i].y = v[j][i].y + p.y;
+            v[j][i].z = v[j][i].z + p.z;
+            v[j][i].w = v[j][i].w + p.w;
+          }
+        }
         if (b2) {  // w * (y + b2[e]): the expert's bias before its routing weight
 #pragma unroll
           for (int i = 0; i < NC; ++i) {
@@ -110,7 +124,7 @@ unsigned grid_for(int64_t work) {
 
 hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
                           const int32_t* topk_ids, int64_t E, int64_t T, int64_t H, int64_t K,
-                          const float* b2, float* out, hipStream_t stream) {
+                          const float* b2, float* out, hipStream_t stream, int ksplit) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
   const int64_t nc = (H / 4 + kThreads - 1) / kThreads;  // float4 columns per lane
@@ -118,7 +132,8 @@ hipError_t launch_combine(const float* y, const float* topk_weights, const int32
   const dim3 grid((unsigned)(T < 2048 ? T : 2048), (unsigned)((nc + 7) / 8));
 #define MOE_COMBINE(KP, NC)                                                                    \
   combine_kernel<KP, NC><<<grid, kThreads, 0, stream>>>(y, topk_weights, slot_of, topk_ids,    \
-                                                        (int32_t)E, T, H, (int32_t)K, b2, out)
+                                                        (int32_t)E, T, H, (int32_t)K, b2, out, \
+                                                        ksplit)
 #define MOE_COMBINE_NC(KP)            \
   do {                                \
     if (nc <= 1) MOE_COMBINE(KP, 1);  \

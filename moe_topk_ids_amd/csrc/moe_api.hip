@@ -158,6 +158,7 @@ struct Layout {
   int path = MOE_PATH_GROUPED;
   bool decode = false;
   moe::GemmCfg g1{}, g2{};
+  int ks2 = 1;  // contraction split of the down projection
   int64_t cap = 0, max_tiles = 0, nblk = 0;
   bool widened = false;       // room for bf16 copies of FP8 weights (grouped path)
   size_t w1dq = 0, w2dq = 0;
@@ -190,6 +191,10 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   }
   L.g1 = moe::pick_gemm1_cfg(T, K, H, I, E);
   L.g2 = moe::pick_gemm2_cfg(n, H, I, E, L.g1.bm);
+  // the atomic combine adds every tile's result to out: no partial sums there
+  L.ks2 = (flags & MOE_FLAG_ATOMIC_COMBINE)
+              ? 1
+              : moe::pick_ksplit(L.g2, T, K, E, (H + L.g2.bn - 1) / L.g2.bn, I);
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
   L.nblk = moe::route_blocks(n);
@@ -201,7 +206,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.slot_of = take((size_t)n * 4);
   L.block_hist = take((size_t)E * L.nblk * 4);
   L.act = take((size_t)L.cap * I * 2);
-  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)n * H * 4);
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)L.ks2 * n * H * 4);
   if ((flags & MOE_FLAG_FP8_WEIGHTS) && fp8_may_widen(T, H, I, E, K)) {
     L.widened = true;
     L.w1dq = take((size_t)E * 2 * I * H * 2);
@@ -419,13 +424,14 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
       float* y = at<float>(ws, L.y);
       st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
                                             tile_expert, num_tiles, topk_weights, H, I, K,
-                                            L.max_tiles, y, nullptr, nullptr, stream)
+                                            L.max_tiles, y, nullptr, nullptr, stream, L.ks2,
+                                            T * K)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, K, L.max_tiles, y, nullptr, nullptr,
-                                        stream);
+                                        stream, L.ks2, T * K);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
       st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2, out,
-                               stream);
+                               stream, L.ks2);
       if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
     }
   }

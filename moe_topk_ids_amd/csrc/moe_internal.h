@@ -65,7 +65,7 @@ hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q
                             const int32_t* tile_expert, const int32_t* num_tiles,
                             const float* topk_weights, int64_t H, int64_t I, int64_t K,
                             int64_t max_tiles, float* y, float* out, const float* b2,
-                            hipStream_t stream);
+                            hipStream_t stream, int ksplit = 1, int64_t n_slots = 0);
 
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
@@ -80,14 +80,21 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
-                        const float* b2, hipStream_t stream);
+                        const float* b2, hipStream_t stream, int ksplit = 1,
+                        int64_t n_slots = 0);
 
-// out[t, :] = sum_k w[t,k] * (y[t*K+k, :] + b2[e_k, :]) (b2 may be null).
+// Split of the down projection's contraction (1, 2 or 4; see gemm.hip):
+// with ksplit > 1, launch_gemm2 writes ksplit partial slot buffers y + s*n_slots*H.
+int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, int64_t kdim);
+
+// out[t, :] = sum_k w[t,k] * (y[t*K+k, :] + b2[e_k, :]) (b2 may be null),
+// where with a split contraction y[f, :] is the sum over s = 0..ksplit-1 (in
+// that order) of the partial rows y + s*T*K*H.
 // A slot is dropped if slot_of[f] < 0, or, without slot_of, if its id is
 // outside [0, E).
 hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
                           const int32_t* topk_ids, int64_t E, int64_t T, int64_t H, int64_t K,
-                          const float* b2, float* out, hipStream_t stream);
+                          const float* b2, float* out, hipStream_t stream, int ksplit = 1);
 hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
 
 // Sets *err_flag to 1 if any id is outside [0, E) or repeats within a token.

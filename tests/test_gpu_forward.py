@@ -5,8 +5,8 @@ import torch
 
 import moe_topk_ids_amd as moe
 import oracle
-from gpu_helpers import (assert_close, cpu_inputs, oracle_rows, rel_l2, require_gpu, sample_rows,
-                         say, shape_inputs, to_device)
+from gpu_helpers import (REL_L2_BF16_INTER, assert_close, cpu_inputs, oracle_rows, rel_l2,
+                         require_gpu, sample_rows, say, shape_inputs, to_device)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -162,6 +162,38 @@ def test_slot_path_is_deterministic_and_permutation_invariant():
         pd[k] = dd[k][perm.cuda()].contiguous()
     c = _run(pd, PATHS["slot"])
     assert np.array_equal(c, a[perm.numpy()])
+
+
+def test_split_down_projection():
+    """Few tokens per expert (the shapes-table row T=135, E=8, top-2): the
+    down projection's contraction is split and the combine adds the partial
+    rows in a fixed order. Against the oracle on every row; bitwise
+    run-to-run and under token permutation (the split is the same for every
+    row)."""
+    require_gpu()
+    T, H, I, E, K = 135, 2048, 2048, 8, 2
+    n = T * K
+    slot_ws = moe.moe_workspace_bytes(T, H, I, E, K, moe.FLAG_FORCE_GROUPED)
+    atomic_ws = moe.moe_workspace_bytes(T, H, I, E, K,
+                                        moe.FLAG_FORCE_GROUPED | moe.FLAG_ATOMIC_COMBINE)
+    # the slot path holds more than one fp32 slot buffer: the split is taken
+    assert slot_ws - atomic_ws > n * H * 4
+    d = cpu_inputs(T, H, I, E, K, seed=135)
+    dd = to_device(d)
+    rows = np.arange(T)
+    a = _run(dd, PATHS["slot"])
+    assert_close(a, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True), "split T=135")
+    b = _run(dd, PATHS["slot"])
+    assert np.array_equal(a, b)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(T))
+    pd = dict(dd)
+    for k in ("hidden_states", "topk_weights", "topk_ids"):
+        pd[k] = dd[k][perm.cuda()].contiguous()
+    c = _run(pd, PATHS["slot"])
+    assert np.array_equal(c, a[perm.numpy()])
+    # the atomic path (no split) stays within the bar of the split path
+    e = _run(dd, PATHS["atomic"])
+    assert rel_l2(e, a) <= REL_L2_BF16_INTER
 
 
 @pytest.mark.parametrize("name", ["prefill", "large"])
