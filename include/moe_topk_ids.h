@@ -202,7 +202,7 @@ int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fla
  *   tile_expert[cap/m_tile]  expert of each m_tile-row tile
  *   num_tiles[1]     offsets[E] / m_tile
  * `capacity` is the length of `sorted`; it must be at least
- * T*K + min(E, T*K)*(m_tile-1). m_tile must be a power of two in [16, 256].
+ * T*K + min(E, T*K)*(m_tile-1). m_tile must be a multiple of 16 in [16, 256].
  * `scratch` is a device buffer of at least moe_route_scratch_bytes(T,K,E)
  * bytes. Deterministic: the output is a pure function of the ids.
  */
@@ -218,8 +218,9 @@ size_t moe_route_scratch_bytes(int64_t T, int64_t K, int64_t E);
  * f = sorted[r] >= 0, act[r, :] = bf16_rne(silu(g) * u) for token f / K and
  * expert tile_expert[r / m_tile]; pad rows get zeros. act is bf16
  * [capacity, I] (row-major); rows >= offsets[E] are not written.
- * `max_tiles` = capacity / m_tile bounds the launch. m_tile must be 64, 128
- * or 256 (the row tiles the grouped GEMMs are built for).
+ * `max_tiles` = capacity / m_tile bounds the launch. m_tile must be 64, 128,
+ * 192 or 256 (the row tiles the grouped GEMMs are built for; moe_m_tile
+ * returns one of them).
  */
 int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    const int32_t* tile_expert, const int32_t* num_tiles,

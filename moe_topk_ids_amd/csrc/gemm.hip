@@ -576,6 +576,7 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   // shape, pipeline depth and wave layout on the workloads' shapes
   if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE, Q>(a, stream);
   if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
+  if (cfg.bm == 192 && cfg.bn == 256) return launch_cfg<192, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   return hipErrorInvalidValue;
 }
@@ -590,12 +591,18 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
 // normal approximation. A product's time is then taken as (tiles per CU) x
 // (flops per tile) / (relative tile efficiency). 64x256 and 128x128 tiles
 // run two workgroups per CU, so their tail rounds overlap and the count
-// stays fractional; a 256x256 tile fills a CU alone, so it is rounded up to
-// whole rounds. The efficiencies (64x256 0.91, 128x128 1, 256x256 1.23)
-// were fitted to measured times of all three configurations on every shape
-// of the atrex-bench shapes table; against the fastest configuration per
-// shape the model gives up at most 1-2 % except in the weight-streaming
-// corner (E=128, I=384, ~32 rows per expert), where 128x128 is 10 % faster.
+// stays fractional; 192x256 and 256x256 tiles fill a CU alone, so they are
+// rounded up to whole rounds. The efficiencies (64x256 0.91, 128x128 1,
+// 256x256 1.23) were fitted to measured times of those three
+// configurations on every shape of the atrex-bench shapes table; against
+// the fastest configuration per shape the model gives up at most 1-2 %
+// except in the weight-streaming corner (E=128, I=384, ~32 rows per
+// expert), where 128x128 is 10 % faster. 192x256 (0.9 the padding of
+// 256-row tiles on ~1050-row experts, and exactly three rounds for the
+// prefill shape) takes 1.15: with it the model picks 192x256 where it
+// measured fastest (T=4195 and T=4098 with E=8, T=2400 with E=128: 12-19 %
+// less than the previous pick) and keeps 256x256 where that stays ahead
+// (T >= 8192 with E=128, the large E=8 shapes).
 namespace {
 double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
   const int64_t n = T * K;
@@ -615,14 +622,14 @@ double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
 }
 
 double model_cost(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E, GemmCfg c) {
-  const double eff = c.bm == 64 ? 0.91 : c.bm == 128 ? 1.0 : 1.23;
+  const double eff = c.bm == 64 ? 0.91 : c.bm == 128 ? 1.0 : c.bm == 192 ? 1.15 : 1.23;
   const double rt = expected_row_tiles(T, K, E, c.bm);
   const double prod[2][2] = {{(double)H, (double)(2 * I / c.bn)},                  // gate/up
                              {(double)I, (double)((H + c.bn - 1) / c.bn)}};  // down
   double t = 0.0;
   for (int g = 0; g < 2; ++g) {
     const double per_cu = rt * prod[g][1] / 256.0;
-    const double rounds = c.bm == 256 ? fmax(1.0, ceil(per_cu - 0.02)) : fmax(1.0, per_cu);
+    const double rounds = c.bm >= 192 ? fmax(1.0, ceil(per_cu - 0.02)) : fmax(1.0, per_cu);
     t += rounds * (double)c.bm * c.bn * prod[g][0] * 2.0 / eff;
   }
   return t;
@@ -630,7 +637,7 @@ double model_cost(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E, GemmCfg
 }  // namespace
 
 GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
-  const GemmCfg cands[3] = {{64, 256}, {128, 128}, {256, 256}};
+  const GemmCfg cands[4] = {{64, 256}, {128, 128}, {192, 256}, {256, 256}};
   GemmCfg best = cands[1];
   double best_t = model_cost(T, K, H, I, E, best);
   for (const GemmCfg& c : cands) {
@@ -653,7 +660,7 @@ GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
 // Measured at T = 135: 31 -> 21 us. The gate/up projection is not split:
 // with an extra pass for the activation it measured no faster.
 int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, int64_t kdim) {
-  const int64_t per_cu = cfg.bm == 256 ? 1 : 2;  // LDS-bound residency of the tile shapes
+  const int64_t per_cu = cfg.bm >= 192 ? 1 : 2;  // LDS-bound residency of the tile shapes
   const double slots = 256.0 * per_cu;
   const double tiles = expected_row_tiles(T, K, E, cfg.bm) * (double)n_tiles;
   const int64_t nk = kdim / 64;
@@ -668,6 +675,7 @@ GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm)
   (void)I;
   (void)E;
   if (bm == 256) return GemmCfg{256, 256};
+  if (bm == 192) return GemmCfg{192, 256};
   if (bm == 128) return GemmCfg{128, 128};
   return GemmCfg{64, 256};
 }

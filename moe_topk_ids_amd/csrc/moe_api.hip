@@ -100,7 +100,12 @@ double fp8_widen_us(int64_t H, int64_t I, int64_t E) {
 
 double fp8_in_register_us(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   const int bm = moe::pick_gemm1_cfg(T, K, H, I, E).bm;
-  const double per_gflop = bm == 256 ? kFp8InRegUsPerGflop256 : kFp8InRegUsPerGflop128;
+  // a widened weight fragment serves the wave's token fragments: 4 with
+  // 256-row tiles, 3 with 192-row tiles (scaled from the 2 of the 128-row
+  // measurement; not measured itself), 2 with the two-workgroup tiles
+  const double per_gflop = bm == 256   ? kFp8InRegUsPerGflop256
+                           : bm == 192 ? kFp8InRegUsPerGflop128 * 2.0 / 3.0
+                                       : kFp8InRegUsPerGflop128;
   return per_gflop * 6.0 * (double)T * K * H * I * 1e-9;
 }
 
@@ -511,8 +516,8 @@ int moe_route(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E, int32_t 
   if (E > moe::kMaxExperts)
     return set_error(MOE_ERR_UNSUPPORTED, "num_experts=%lld exceeds %d", (long long)E,
                      moe::kMaxExperts);
-  if (m_tile < 16 || m_tile > 256 || (m_tile & (m_tile - 1)) != 0)
-    return set_error(MOE_ERR_INVALID_ARG, "m_tile=%d must be a power of two in [16, 256]", m_tile);
+  if (m_tile < 16 || m_tile > 256 || m_tile % 16 != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "m_tile=%d must be a multiple of 16 in [16, 256]", m_tile);
   if (T * K > (int64_t)1 << 30)
     return set_error(MOE_ERR_UNSUPPORTED, "T*K=%lld is too large", (long long)(T * K));
   const int64_t n = T * K;
@@ -542,8 +547,9 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    void* stream) {
   int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  if (m_tile != 64 && m_tile != 128 && m_tile != 256)
-    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128 and 256", m_tile);
+  if (m_tile != 64 && m_tile != 128 && m_tile != 192 && m_tile != 256)
+    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128, 192 and 256",
+                     m_tile);
   if (max_tiles < 0 || max_tiles > INT32_MAX)
     return set_error(MOE_ERR_INVALID_ARG, "max_tiles=%lld", (long long)max_tiles);
   if (T == 0 || max_tiles == 0) return MOE_OK;
@@ -562,8 +568,9 @@ int moe_gemm1_silu_fp8(const void* hidden, const uint8_t* w1q, const float* w1_s
                        int64_t K, int32_t m_tile, int64_t max_tiles, void* act, void* stream) {
   int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
-  if (m_tile != 64 && m_tile != 128 && m_tile != 256)
-    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128 and 256", m_tile);
+  if (m_tile != 64 && m_tile != 128 && m_tile != 192 && m_tile != 256)
+    return set_error(MOE_ERR_UNSUPPORTED, "m_tile=%d: the GEMM supports 64, 128, 192 and 256",
+                     m_tile);
   if (!moe::fp8_block_ok(H, I, block) || !moe::fp8_gemm_supported(H, I, block))
     return set_error(MOE_ERR_UNSUPPORTED,
                      "scale block %lld: needs a multiple of 128 dividing H=%lld and I=%lld, "

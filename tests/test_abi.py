@@ -114,7 +114,9 @@ def test_fp8_argument_validation(lib):
 
 def test_route_argument_validation(lib):
     p = ctypes.c_void_p(0)
-    assert lib.moe_route(p, 4, 2, 8, 48, p, p, p, p, p, p, 1000, p, p) == moe.MOE_ERR_INVALID_ARG
+    # m_tile must be a multiple of 16 in [16, 256]
+    for m in (8, 40, 272):
+        assert lib.moe_route(p, 4, 2, 8, m, p, p, p, p, p, p, 1000, p, p) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(p, 4, 2, 8, 64, p, p, p, p, p, p, 10, p, p) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_gemm1_silu(p, p, p, p, p, 4, 128, 128, 8, 2, 32, 1, p, p) == moe.MOE_ERR_UNSUPPORTED
 
@@ -134,7 +136,7 @@ def test_workspace_and_tile_queries(lib):
     ws_atomic = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, moe.FLAG_ATOMIC_COMBINE)
     # the slot path holds the fp32 per-slot outputs [T*K, H]
     assert ws_slot - ws_atomic >= 4195 * 2 * 2048 * 4
-    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128, 256)
+    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128, 192, 256)
     assert moe.moe_uses_decode_path(1, 2048, 768, 128, 8)
     assert not moe.moe_uses_decode_path(4195, 2048, 2048, 8, 2)
     assert moe.moe_uses_decode_path(4195, 2048, 2048, 8, 2, moe.FLAG_FORCE_DECODE)
@@ -147,10 +149,13 @@ def test_tile_choice(lib):
     # the cost model's picks on shapes where the measured winner is clear
     assert moe.moe_m_tile(135, 2048, 2048, 8, 2) == 128    # few rows: more tiles in flight
     assert moe.moe_m_tile(668, 2048, 2048, 8, 2) == 64     # ~167 rows per expert: least padding
-    assert moe.moe_m_tile(2400, 2048, 768, 128, 8) == 64
     assert moe.moe_m_tile(8192, 4096, 384, 128, 8) == 256  # many tiles: the big tile's efficiency
     assert moe.moe_m_tile(15381, 4096, 4096, 8, 2) == 256
-    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128)  # 256-row tiles leave a tail round
+    # ~1050 rows per expert: 192-row tiles pad like 128-row ones (256-row
+    # tiles pad to 1280) and make exactly three rounds; measured fastest
+    assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) == 192
+    assert moe.moe_m_tile(4098, 4096, 4096, 8, 2) == 192
+    assert moe.moe_m_tile(2400, 2048, 768, 128, 8) == 192  # ~150 rows per expert: one tile each
 
 
 def test_path_choice(lib):

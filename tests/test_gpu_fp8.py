@@ -132,17 +132,19 @@ def test_fp8_grouped_at_the_scale_block_limit(H, I, block, native):
     _check(got, want, tight, f"fp8/grouped H={H} I={I}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "wide"])
-def test_fp8_gemm1_intermediate(name):
+@pytest.mark.parametrize("name,m_tile", [("tiny", None), ("wide", None), ("tiny", 192),
+                                         ("tiny", 64)])
+def test_fp8_gemm1_intermediate(name, m_tile):
     """moe_gemm1_silu_fp8 (codes widened in registers) vs the oracle's per-slot
     bf16 activation on the bf16-widened weights: at most one bf16 ulp apart
-    (the k order inside a stage differs), nearly all identical."""
+    (the k order inside a stage differs), nearly all identical. At the
+    workload's own row tile and at the other tile shapes."""
     require_gpu()
     s = SHAPES[name]
     d = shape_inputs(name)
     q = make_fp8_weights(d, 128)
     dd, qd = to_device(d), _to_dev(q)
-    M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
+    M = m_tile or moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
     say(f"fp8 intermediate {name} M={M}")
     r = moe.moe_route(dd["topk_ids"], s.E, M)
     act = moe.moe_gemm1_silu_fp8(dd["hidden_states"], qd["w1q"], qd["w1s"], 128, r, s.K, M)

@@ -35,7 +35,7 @@ def test_route_bitexact_on_workloads(name):
     ids = shape_inputs(name)["topk_ids"].numpy()
     M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
     _check_route(ids, s.E, M, name)
-    for other in (64, 128):
+    for other in (64, 128, 192):
         if other != M:
             _check_route(ids, s.E, other, f"{name} M={other}")
 
