@@ -653,20 +653,20 @@ GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
 // Split of the down projection's contraction for problems whose tiles
 // cannot fill the chip (few tokens per expert: at T = 135, E = 8, top-2 its
 // 128 tiles would occupy a quarter of the workgroup slots, each a chain of
-// 32 dependent stages). Splitting into S parts gives S times the tiles, each
-// with 1/S of the chain; the combine adds the S partial rows in a fixed
-// order (deterministic). S is the largest of 1, 2, 4 with S * tiles within
-// the workgroups the chip holds at once, and at least 4 stages per split.
-// Measured at T = 135: 31 -> 21 us. The gate/up projection is not split:
-// with an extra pass for the activation it measured no faster.
+// 32 dependent stages). Splitting it in two gives twice the tiles, each
+// with half the chain; the combine adds the two partial rows in a fixed
+// order (deterministic). Taken while the doubled tile count stays within the
+// workgroups the chip holds at once and each half keeps at least 4 stages.
+// Measured with the weights streamed from HBM, 128-row tiles: T = 135
+// 32.1 -> 22.9 us, T = 277 33.6 -> 25.9 us; four parts measured slower
+// (26.2, 30.5 us). The gate/up projection is not split: with an extra pass
+// for the activation it measured no faster.
 int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, int64_t kdim) {
   const int64_t per_cu = cfg.bm >= 192 ? 1 : 2;  // LDS-bound residency of the tile shapes
   const double slots = 256.0 * per_cu;
   const double tiles = expected_row_tiles(T, K, E, cfg.bm) * (double)n_tiles;
   const int64_t nk = kdim / 64;
-  int s = 1;
-  while (s < 4 && tiles * 2 * s <= slots && nk % (2 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
-  return s;
+  return (tiles * 2 <= slots && nk % 2 == 0 && nk / 2 >= 4) ? 2 : 1;
 }
 
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm) {

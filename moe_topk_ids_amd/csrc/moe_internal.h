@@ -83,7 +83,7 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const float* b2, hipStream_t stream, int ksplit = 1,
                         int64_t n_slots = 0);
 
-// Split of the down projection's contraction (1, 2 or 4; see gemm.hip):
+// Split of the down projection's contraction (1 or 2; see gemm.hip):
 // with ksplit > 1, launch_gemm2 writes ksplit partial slot buffers y + s*n_slots*H.
 int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, int64_t kdim);
 
