@@ -309,8 +309,9 @@ def test_caller_workspace_and_side_stream():
 
 
 def test_decode_path_with_caller_workspace_of_garbage():
-    """The small-batch path with a caller workspace full of arbitrary bytes
-    gives the internal-workspace result, twice in a row."""
+    """The decode path with a caller workspace full of arbitrary bytes (its
+    readiness counters included) gives the internal-workspace result, twice
+    in a row."""
     require_gpu()
     s = SHAPES["decode"]
     dd = to_device(shape_inputs("decode"))
@@ -326,9 +327,9 @@ def test_decode_path_with_caller_workspace_of_garbage():
 
 
 def test_decode_after_grouped_calls_and_back_to_back():
-    """Grouped calls between small-batch calls share the internal workspace;
-    40 small-batch calls queued without a host sync all give the same bits;
-    so does the debug-sync flag."""
+    """Grouped calls between decode calls share the internal workspace; 40
+    decode calls queued without a host sync (each advancing the readiness
+    counters) all give the same bits; so does the debug-sync flag."""
     require_gpu()
     dd = to_device(shape_inputs("decode"))
     tiny = to_device(shape_inputs("tiny"))
@@ -341,6 +342,25 @@ def test_decode_after_grouped_calls_and_back_to_back():
     for o in outs:
         assert np.array_equal(o.cpu().numpy(), ref)
     assert np.array_equal(_run(dd, moe.FLAG_DEBUG_SYNC), ref)
+
+
+@pytest.mark.parametrize("shape", [(2048, 768, 128, 8), (2048, 2048, 8, 2), (512, 256, 8, 2)])
+def test_decode_tokens_are_independent(shape):
+    """On the decode path each output row depends on its own token only: token
+    0 gives the same bits alone and beside a second token, and both rows
+    match the oracle."""
+    require_gpu()
+    H, I, E, K = shape
+    d = cpu_inputs(2, H, I, E, K, seed=11)
+    dd = to_device(d)
+    fl = moe.FLAG_FORCE_DECODE
+    two = _run(dd, fl)
+    one = _run({k: (v[:1] if k in ("hidden_states", "topk_weights", "topk_ids") else v)
+                for k, v in dd.items()}, fl)
+    assert np.array_equal(one[0], two[0])
+    rows = np.arange(2)
+    assert_close(two, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"decode-two-tokens/{shape}")
 
 
 def test_debug_sync_flag():
