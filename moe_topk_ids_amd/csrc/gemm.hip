@@ -44,7 +44,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -106,37 +105,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Buffer resource for raw (unstructured) loads: bytes past num_records read
 // as zero, which is how pad rows and out-of-range weight rows are zero-filled
 // without branches.
-__device__ __forceinline__ int32x4_t make_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  int32x4_t r;
-  r[0] = (int32_t)(uint32_t)a;
-  r[1] = (int32_t)(uint32_t)(a >> 32) & 0xffff;  // stride 0
-  r[2] = (int32_t)num_records;
-  r[3] = 0x00020000;
-  return r;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records,
+                                           0x00020000);
 }
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= num_records reads zeros
 
-// One 16-byte load per lane straight into LDS: lane i's bytes land at
-// lds_addr + 16*i. lds_addr must be wave-uniform.
-__device__ __forceinline__ void load_lds_b128(int32x4_t rsrc, uint32_t voffset, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-      : "memory", "m0");
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte load per lane straight into LDS (buffer_load_dwordx4 with the
+// LDS bit): lane i's bytes land at dst + 16*i, read from voffset + soffset.
+// dst must be wave-uniform. (Plain functions: called from a template-
+// dependent context, the builtin makes the host pass drop the kernel.)
+__device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t rsrc, const char* dst,
+                                              uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, voffset, soffset, 0, 0);
 }
 
-// One 4-byte load per lane into LDS: lane i's word lands at lds_addr + 4*i.
-__device__ __forceinline__ void load_lds_b32(int32x4_t rsrc, uint32_t voffset, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds"
-      :
-      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-      : "memory", "m0");
+// One 4-byte load per lane into LDS: lane i's word lands at dst + 4*i.
+__device__ __forceinline__ void load_lds_b32(__amdgpu_buffer_rsrc_t rsrc, const char* dst,
+                                             uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, voffset, 0, 0, 0);
 }
 
 // 8 OCP E4M3 codes (k order: the bytes of lo, then of hi) to bf16 as
@@ -300,7 +291,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS load bases in M0
   const int wm = wave % WGM;
   const int wn = wave / WGM;
 
@@ -357,8 +348,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const char* b_base = Q ? reinterpret_cast<const char*>(args.wq) + (int64_t)e * args.w_expert_stride
                          : reinterpret_cast<const char*>(args.w + (int64_t)e * args.w_expert_stride);
   const uint32_t b_num = (uint32_t)(args.w_expert_stride * (Q ? 1 : 2));
-  const int32x4_t rsrc_a = make_rsrc(a_base, a_num);
-  const int32x4_t rsrc_b = make_rsrc(b_base, b_num);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a_base, a_num);
+  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(b_base, b_num);
   // token rows of the tile's slots: every lookup issued before the first
   // use, offsets computed without branches
   int32_t fsl[LA];
@@ -384,7 +375,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     const int64_t row = weight_row(n);
     boff[j] = row >= 0 ? (uint32_t)(row * kdim * (Q ? 1 : 2)) + cb : kOutOfRange;
   }
-  const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
   // fp8 weights: the tile's scales go to LDS ahead of stage 0's loads (and
   // so have landed once stage 0 has: loads complete in issue order)
@@ -393,15 +383,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     const int nqb = args.nqb;
     sst = nqb | 1;
     const int64_t rows_pe = args.w_expert_stride / kdim;
-    const int32x4_t rsrc_s =
+    const __amdgpu_buffer_rsrc_t rsrc_s =
         make_rsrc(args.wscale + (int64_t)e * rows_pe * nqb, (uint32_t)(rows_pe * nqb * 4));
-    const uint32_t scl_base = (uint32_t)reinterpret_cast<uintptr_t>(scl);
     for (int p0 = wave * 64; p0 < BN * sst; p0 += NW * 64) {
       const int p = p0 + lane;
       const int n = p / sst, b = p - n * sst;
       const int64_t row = n < BN ? weight_row(n) : -1;
       const uint32_t off = (row >= 0 && b < nqb) ? (uint32_t)((row * nqb + b) * 4) : kOutOfRange;
-      load_lds_b32(rsrc_s, off, __builtin_amdgcn_readfirstlane(scl_base + (uint32_t)p0 * 4));
+      load_lds_b32(rsrc_s, reinterpret_cast<const char*>(scl) + p0 * 4, off);
     }
   }
 
@@ -428,15 +417,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int nk = (int)(kdim / BK) / args.ksplit;  // stages of this split
   const int kt0 = split * nk;                     // its first stage
 
+  // Loads of stage kt into LDS buffer `buf`; stages past the last one read
+  // out of range (nothing is fetched, the buffer, which is not read again,
+  // receives zeros), so the issue needs no branch.
 #define MOE_ISSUE_STAGE(buf, kt)                                                              \
   do {                                                                                        \
-    const uint32_t sb = smem_base + (uint32_t)(buf) * STAGE;                                  \
+    const bool live_ = (kt) < nk;                                                             \
+    const uint32_t sa_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWB : kOutOfRange;                 \
+    const uint32_t sw_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWW : kOutOfRange;                 \
+    const char* sb_ = smem + (buf) * STAGE;                                                   \
     _Pragma("unroll") for (int j = 0; j < LA; ++j)                                           \
-        load_lds_b128(rsrc_a, aoff[j] + (uint32_t)(kt0 + (kt)) * ROWB,                        \
-                      __builtin_amdgcn_readfirstlane(sb + (wave * LA + j) * 1024));           \
+        load_lds_b128(rsrc_a, sb_ + (wave * LA + j) * 1024, aoff[j], sa_);                    \
     _Pragma("unroll") for (int j = 0; j < LB; ++j)                                           \
-        load_lds_b128(rsrc_b, boff[j] + (uint32_t)(kt0 + (kt)) * ROWW,                        \
-                      __builtin_amdgcn_readfirstlane(sb + A_BYTES + (wave * LB + j) * 1024)); \
+        load_lds_b128(rsrc_b, sb_ + A_BYTES + (wave * LB + j) * 1024, boff[j], sw_);          \
   } while (0)
 
   // Fragment reads of sub-step kk of stage kt (in LDS buffer `buf`); the
@@ -494,57 +487,75 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 
   constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
   static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
+  static_assert(NS == 2, "two-stage ring");
+  // Matrix ops of a stage's last sub-step issued ahead of the stage
+  // boundary: a quarter of them in the bf16 gate/up product with 256-row
+  // tiles (measured 3-4 % faster there); elsewhere none (equal or slower).
+  constexpr int PRE = (Q || MODE != kGateUpSilu || BM != 256) ? 0 : TM * TN / 4;
 
-  // prologue: stages 0..NS-1 in flight (one per buffer), stage 0 landed,
-  // its first fragments read
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < nk) MOE_ISSUE_STAGE(s, s);
-  if (NS <= nk) wait_vmcnt<(NS - 1) * (LA + LB)>();
-  else wait_vmcnt<0>();
+  // matrix ops [first, first + count) of one sub-step (op i: weight sub-tile
+  // i / TM, token sub-tile i % TM)
+#define MOE_MMA(F, first, count)                                                               \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM * TN; ++i_) {                                   \
+      if (i_ >= (first) && i_ < (first) + (count)) {                                           \
+        const int tn_ = i_ / TM, tm_ = i_ % TM;                                                \
+        acc[tn_][tm_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[tn_], F##b[tm_],         \
+                                                                acc[tn_][tm_], 0, 0, 0);       \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
+  // sub-steps 0 .. KK-2 of stage kt: the fragments of the next sub-step are
+  // read (and fp8 codes widened) around this sub-step's matrix ops
+#define MOE_SUBSTEPS(buf, kt)                                                                  \
+  do {                                                                                         \
+    _Pragma("unroll") for (int kk = 0; kk + 1 < KK; ++kk) {                                    \
+      if (kk % 2 == 0) {                                                                       \
+        MOE_LOAD_FRAGS(f1, buf, kk + 1, kt);                                                   \
+        MOE_MMA(f0, 0, TM * TN);                                                               \
+        MOE_WIDEN(f1, kk + 1);                                                                 \
+      } else {                                                                                 \
+        MOE_LOAD_FRAGS(f0, buf, kk + 1, kt);                                                   \
+        MOE_MMA(f1, 0, TM * TN);                                                               \
+        MOE_WIDEN(f0, kk + 1);                                                                 \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
+
+  // prologue: stages 0 and 1 in flight (one per buffer; a missing stage 1
+  // reads out of range), stage 0 landed, its first fragments read
+  MOE_ISSUE_STAGE(0, 0);
+  MOE_ISSUE_STAGE(1, 1);
+  wait_vmcnt<LA + LB>();
   __syncthreads();
   bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
   MOE_LOAD_FRAGS(f0, 0, 0, 0);
   MOE_WIDEN(f0, 0);
 
-  // Steady state. Fragments of the next sub-step are read before the matrix
-  // ops of the current one. In the last sub-step of a stage its fragments
-  // are already in registers, so the wait for stage kt+1, the barrier, the
-  // issue of stage kt+NS into the buffer stage kt leaves free, and the reads
-  // of stage kt+1's first fragments all overlap that sub-step's matrix ops.
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % NS;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bool more = kk + 1 < KK || kt + 1 < nk;
-      if (kk + 1 < KK) {
-        if (kk % 2 == 0) MOE_LOAD_FRAGS(f1, buf, kk + 1, kt);
-        else MOE_LOAD_FRAGS(f0, buf, kk + 1, kt);
-      } else if (kt + 1 < nk) {
-        // issued so far: stages 0 .. min(kt+NS-1, nk-1); stage kt+1 must have landed
-        if (kt + NS - 1 < nk) wait_vmcnt<(NS - 2) * (LA + LB)>();
-        else wait_vmcnt<0>();
-        __syncthreads();  // stage kt+1 visible to all; every wave is done reading stage kt
-        if (kt + NS < nk) MOE_ISSUE_STAGE(buf, kt + NS);
-        MOE_LOAD_FRAGS(f0, (kt + 1) % NS, 0, kt + 1);
-      }
-      if (kk % 2 == 0) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0a[tn], f0b[tm], acc[tn][tm], 0, 0, 0);
-        if (more) MOE_WIDEN(f1, (kk + 1) % KK);
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1a[tn], f1b[tm], acc[tn][tm], 0, 0, 0);
-        if (more) MOE_WIDEN(f0, (kk + 1) % KK);
-      }
-    }
+  // Every stage but the last. Its last sub-step's fragments are already in
+  // registers, so the stage boundary is interleaved with that sub-step's
+  // matrix ops: the first PRE of them, then the wait (stage kt+1 landed: it
+  // is the only stage in flight) and the barrier (every wave is done reading
+  // stage kt), then the loads of stage kt+2 into the buffer stage kt leaves
+  // (issued first: they have the longest way to go), the reads of stage
+  // kt+1's first fragments, then the rest of the matrix ops. The last stage
+  // is peeled off, so the loop body has no branch (with one, the
+  // accumulators are copied between register files around it).
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int buf = kt & 1;
+    MOE_SUBSTEPS(buf, kt);
+    MOE_MMA(f1, 0, PRE);
+    wait_vmcnt<0>();
+    __syncthreads();
+    MOE_ISSUE_STAGE(buf, kt + 2);
+    MOE_LOAD_FRAGS(f0, buf ^ 1, 0, kt + 1);
+    MOE_MMA(f1, PRE, TM * TN - PRE);
+    MOE_WIDEN(f0, 0);
   }
+  MOE_SUBSTEPS((nk - 1) & 1, nk - 1);
+  MOE_MMA(f1, 0, TM * TN);
+#undef MOE_SUBSTEPS
+#undef MOE_MMA
 #undef MOE_WIDEN
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
