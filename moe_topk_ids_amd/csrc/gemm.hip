@@ -7,9 +7,11 @@
 //
 // A workgroup owns one BM x BN output tile of one expert: BM consecutive rows
 // of the expert-grouped padded layout produced by the routing step (all rows
-// of a tile belong to one expert), and BN weight rows. The grid is sized for
-// the largest possible number of row tiles; workgroups past the device-side
-// tile count exit at once, so no host synchronisation is needed.
+// of a tile belong to one expert), and BN weight rows. The tile list is
+// sized for the largest possible number of row tiles; tiles past the
+// device-side tile count are skipped, so no host synchronisation is needed.
+// The launch is persistent: as many workgroups as the chip holds at once,
+// each looping over tiles.
 //
 // The matrix-core instruction is v_mfma_f32_32x32x16_bf16 with the WEIGHT
 // fragment as its first operand and the TOKEN fragment as its second, so the
@@ -68,6 +70,7 @@ struct GemmArgs {
   int32_t n_tiles;          // weight-row tiles
   int32_t group_m;          // row tiles per scheduling group
   int32_t xcd_slots;        // workgroups resident at once on one XCD
+  int32_t nvb;              // virtual workgroups (tiles of the grid before persistence)
   // split of the down projection's contraction: split s of ksplit covers
   // stages [s*nk/ksplit, (s+1)*nk/ksplit) and writes its partial slot rows
   // to out + s*part_stride
@@ -295,6 +298,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int wm = wave % WGM;
   const int wn = wave / WGM;
 
+  // Persistent: the grid holds what the chip keeps resident, and each
+  // workgroup walks the virtual workgroup ids vb = blockIdx.x, blockIdx.x +
+  // gridDim.x, ... (gridDim.x is a multiple of 8, so every step stays on the
+  // same XCD). A tile's first loads are then issued while the previous tile's
+  // stores drain, instead of after the workgroup slot is freed and
+  // dispatched again. The barrier at the top keeps the previous tile's last
+  // LDS reads ahead of the next tile's loads.
+  for (int vb = blockIdx.x; vb < args.nvb; vb += gridDim.x) {
+  __syncthreads();
+
   // XCD-aware tile order. Logical tiles are ordered in groups of GM row
   // tiles that sweep the weight tiles. Consecutive workgroup ids are dealt
   // round-robin to the 8 XCDs, so the workgroup in slot s of XCD x takes
@@ -308,13 +321,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int per_split = args.max_tiles * n_tiles;
   const int total = per_split * args.ksplit;
   const int S = args.xcd_slots;
-  const int slot = blockIdx.x / 8;
+  const int slot = vb / 8;
   const int nfull = total / (8 * S);
   const int pid = slot < nfull * S
-                      ? (slot / S) * 8 * S + (blockIdx.x % 8) * S + slot % S
-                      : nfull * 8 * S + (blockIdx.x % 8) * ((total - nfull * 8 * S + 7) / 8) +
+                      ? (slot / S) * 8 * S + (vb % 8) * S + slot % S
+                      : nfull * 8 * S + (vb % 8) * ((total - nfull * 8 * S + 7) / 8) +
                             (slot - nfull * S);
-  if (pid >= total) return;
+  if (pid >= total) continue;
   const int split = pid / per_split;  // the contraction split is the slowest index
   const int tpid = pid - split * per_split;
   const int group = tpid / (args.group_m * n_tiles);
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   const int within = tpid - group * args.group_m * n_tiles;
   const int mt = first_m + within % gsize;
   const int ntile = within / gsize;
-  if (mt >= args.num_tiles[0]) return;
+  if (mt >= args.num_tiles[0]) continue;
   const int e = args.tile_expert[mt];
   const int64_t m0 = (int64_t)mt * BM;
   const int64_t kdim = args.kdim;
@@ -561,6 +574,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #undef MOE_ISSUE_STAGE
 
   tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane, split);
+  }  // persistent tile loop
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE, bool Q>
@@ -575,8 +589,12 @@ hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   a.xcd_slots = (int32_t)(32 * (per_cu < 1 ? 1 : per_cu));
   const int64_t S = a.xcd_slots, nfull = total / (8 * S);
   const int64_t blocks = 8 * (nfull * S + (total - nfull * 8 * S + 7) / 8);
+  // virtual workgroups: the tile order's grid; launched: what one round of
+  // the chip holds (both multiples of 8)
+  a.nvb = (int32_t)blocks;
+  const int64_t grid = blocks < 8 * S ? blocks : 8 * S;
   grouped_gemm<BM, BN, BK, WGM, WGN, NS, MODE, Q>
-      <<<dim3((unsigned)blocks), dim3(64 * WGM * WGN), scl_bytes, stream>>>(a);
+      <<<dim3((unsigned)grid), dim3(64 * WGM * WGN), scl_bytes, stream>>>(a);
   return hipGetLastError();
 }
 

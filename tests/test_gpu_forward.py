@@ -164,14 +164,16 @@ def test_slot_path_is_deterministic_and_permutation_invariant():
     assert np.array_equal(c, a[perm.numpy()])
 
 
-def test_split_down_projection():
-    """Few tokens per expert (the shapes-table row T=135, E=8, top-2): the
-    down projection's contraction is split and the combine adds the partial
-    rows in a fixed order. Against the oracle on every row; bitwise
-    run-to-run and under token permutation (the split is the same for every
-    row)."""
+@pytest.mark.parametrize("T,H,I,E,K", [
+    (135, 2048, 2048, 8, 2),  # the shapes-table row: 16 stages per split
+    (96, 1024, 640, 8, 2),    # 5 stages per split: an odd count through the GEMM loop
+])
+def test_split_down_projection(T, H, I, E, K):
+    """Few tokens per expert: the down projection's contraction is split and
+    the combine adds the partial rows in a fixed order. Against the oracle on
+    every row; bitwise run-to-run and under token permutation (the split is
+    the same for every row)."""
     require_gpu()
-    T, H, I, E, K = 135, 2048, 2048, 8, 2
     n = T * K
     slot_ws = moe.moe_workspace_bytes(T, H, I, E, K, moe.FLAG_FORCE_GROUPED)
     atomic_ws = moe.moe_workspace_bytes(T, H, I, E, K,
@@ -182,7 +184,8 @@ def test_split_down_projection():
     dd = to_device(d)
     rows = np.arange(T)
     a = _run(dd, PATHS["slot"])
-    assert_close(a, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True), "split T=135")
+    assert_close(a, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+                 f"split T={T} I={I}")
     b = _run(dd, PATHS["slot"])
     assert np.array_equal(a, b)
     perm = torch.from_numpy(np.random.default_rng(5).permutation(T))
