@@ -306,274 +306,276 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   // dispatched again. The barrier at the top keeps the previous tile's last
   // LDS reads ahead of the next tile's loads.
   for (int vb = blockIdx.x; vb < args.nvb; vb += gridDim.x) {
-  __syncthreads();
-
-  // XCD-aware tile order. Logical tiles are ordered in groups of GM row
-  // tiles that sweep the weight tiles. Consecutive workgroup ids are dealt
-  // round-robin to the 8 XCDs, so the workgroup in slot s of XCD x takes
-  // tile w*8S + x*S + s%S of window w = s/S, S being the workgroups one XCD
-  // holds at once: the XCDs work through the same window of 8S tiles
-  // together (one expert's weights and token rows, which the last-level
-  // cache then serves to all of them), each on a contiguous run of S tiles
-  // that share rows in its own L2. The last, partial window is shared out
-  // evenly over the XCDs.
-  const int n_tiles = args.n_tiles;
-  const int per_split = args.max_tiles * n_tiles;
-  const int total = per_split * args.ksplit;
-  const int S = args.xcd_slots;
-  const int slot = vb / 8;
-  const int nfull = total / (8 * S);
-  const int pid = slot < nfull * S
-                      ? (slot / S) * 8 * S + (vb % 8) * S + slot % S
-                      : nfull * 8 * S + (vb % 8) * ((total - nfull * 8 * S + 7) / 8) +
-                            (slot - nfull * S);
-  if (pid >= total) continue;
-  const int split = pid / per_split;  // the contraction split is the slowest index
-  const int tpid = pid - split * per_split;
-  const int group = tpid / (args.group_m * n_tiles);
-  const int first_m = group * args.group_m;
-  const int gsize = min(args.max_tiles - first_m, args.group_m);
-  const int within = tpid - group * args.group_m * n_tiles;
-  const int mt = first_m + within % gsize;
-  const int ntile = within / gsize;
-  if (mt >= args.num_tiles[0]) continue;
-  const int e = args.tile_expert[mt];
-  const int64_t m0 = (int64_t)mt * BM;
-  const int64_t kdim = args.kdim;
-
-  // weight row (within the expert) of staged row n of this tile, or -1
-  auto weight_row = [&](int n) -> int64_t {
-    if (MODE == kGateUpSilu) {
-      const int64_t n0g = (int64_t)ntile * (BN / 2);
-      return n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
-    }
-    const int64_t row = (int64_t)ntile * BN + n;
-    return row < args.n_out ? row : -1;
-  };
-
-  // ---- per-lane load offsets (fixed over the K loop) ----
-  // load j of this wave covers staged rows RPL*g .. RPL*g+RPL-1 (g = wave*L
-  // + j); lane -> row RPL*g + lane/CPR, physical chunk lane%CPR, logical
-  // chunk (lane%CPR) ^ swz(row): the XOR layout is applied on the global side.
-  uint32_t aoff[LA], boff[LB];
-  const uint16_t* a_base = MODE == kGateUpSilu ? args.a : args.a + m0 * kdim;
-  const uint32_t a_num = MODE == kGateUpSilu ? args.a_bytes : (uint32_t)(BM * kdim * 2);
-  const char* b_base = Q ? reinterpret_cast<const char*>(args.wq) + (int64_t)e * args.w_expert_stride
-                         : reinterpret_cast<const char*>(args.w + (int64_t)e * args.w_expert_stride);
-  const uint32_t b_num = (uint32_t)(args.w_expert_stride * (Q ? 1 : 2));
-  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a_base, a_num);
-  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(b_base, b_num);
-  // token rows of the tile's slots: every lookup issued before the first
-  // use, offsets computed without branches
-  int32_t fsl[LA];
-#pragma unroll
-  for (int j = 0; j < LA; ++j)
-    fsl[j] = MODE == kGateUpSilu ? args.sorted[m0 + RPL * (wave * LA + j) + lane / CPR] : 0;
-#pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    const int r = RPL * (wave * LA + j) + lane / CPR;
-    const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(r)) * 16);
-    if (MODE == kGateUpSilu) {
-      const int32_t f = fsl[j];
-      const uint32_t t = (uint32_t)(f >= 0 ? f : 0) / (uint32_t)args.topk;
-      aoff[j] = f >= 0 ? t * (uint32_t)(kdim * 2) + cb : kOutOfRange;
-    } else {
-      aoff[j] = (uint32_t)(r * kdim * 2) + cb;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < LB; ++j) {
-    const int n = RPW * (wave * LB + j) + lane / CPW;
-    const uint32_t cb = (uint32_t)(((lane % CPW) ^ swz<CPW>(n)) * 16);
-    const int64_t row = weight_row(n);
-    boff[j] = row >= 0 ? (uint32_t)(row * kdim * (Q ? 1 : 2)) + cb : kOutOfRange;
-  }
-
-  // fp8 weights: the tile's scales go to LDS ahead of stage 0's loads (and
-  // so have landed once stage 0 has: loads complete in issue order)
-  int sst = 1;
-  if constexpr (Q) {
-    const int nqb = args.nqb;
-    sst = nqb | 1;
-    const int64_t rows_pe = args.w_expert_stride / kdim;
-    const __amdgpu_buffer_rsrc_t rsrc_s =
-        make_rsrc(args.wscale + (int64_t)e * rows_pe * nqb, (uint32_t)(rows_pe * nqb * 4));
-    for (int p0 = wave * 64; p0 < BN * sst; p0 += NW * 64) {
-      const int p = p0 + lane;
-      const int n = p / sst, b = p - n * sst;
-      const int64_t row = n < BN ? weight_row(n) : -1;
-      const uint32_t off = (row >= 0 && b < nqb) ? (uint32_t)((row * nqb + b) * 4) : kOutOfRange;
-      load_lds_b32(rsrc_s, reinterpret_cast<const char*>(scl) + p0 * 4, off);
-    }
-  }
-
-  // LDS row of each of this wave's weight sub-tiles
-  int nrow[TN];
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    if (MODE == kGateUpSilu) {
-      nrow[tn] = tn < TN / 2 ? wn * (WTN / 2) + tn * 32
-                             : BN / 2 + wn * (WTN / 2) + (tn - TN / 2) * 32;
-    } else {
-      nrow[tn] = wn * WTN + tn * 32;
-    }
-  }
-
-  f32x16_t acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  const int nk = (int)(kdim / BK) / args.ksplit;  // stages of this split
-  const int kt0 = split * nk;                     // its first stage
-
-  // Loads of stage kt into LDS buffer `buf`; stages past the last one read
-  // out of range (nothing is fetched, the buffer, which is not read again,
-  // receives zeros), so the issue needs no branch.
-#define MOE_ISSUE_STAGE(buf, kt)                                                              \
-  do {                                                                                        \
-    const bool live_ = (kt) < nk;                                                             \
-    const uint32_t sa_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWB : kOutOfRange;                 \
-    const uint32_t sw_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWW : kOutOfRange;                 \
-    const char* sb_ = smem + (buf) * STAGE;                                                   \
-    _Pragma("unroll") for (int j = 0; j < LA; ++j)                                           \
-        load_lds_b128(rsrc_a, sb_ + (wave * LA + j) * 1024, aoff[j], sa_);                    \
-    _Pragma("unroll") for (int j = 0; j < LB; ++j)                                           \
-        load_lds_b128(rsrc_b, sb_ + A_BYTES + (wave * LB + j) * 1024, boff[j], sw_);          \
-  } while (0)
-
-  // Fragment reads of sub-step kk of stage kt (in LDS buffer `buf`); the
-  // lane holds 8 k values of its row. bf16 weights: chunk 2*kk + lane/32 of
-  // both 128-byte rows. fp8 weights: one 16-byte chunk of a 64-byte weight
-  // row holds 8 codes for each of two sub-steps, so sub-steps 2j and 2j+1
-  // take the two halves of chunk 2j + lane/32, and the token fragment reads
-  // the matching k values (a fixed permutation of k inside the stage, the
-  // same on both operands). Both chunks of a stage are read with its first
-  // sub-step; each sub-step's codes are widened, as bf16(fp32(code) * scale),
-  // after the matrix ops of the sub-step before it have been issued, so the
-  // conversion overlaps them.
-  uint32_t qraw[Q ? 2 : 1][Q ? TN : 1][4];
-  float qsc[Q ? TN : 1];
-#define MOE_LOAD_FRAGS(F, buf, kk, ktv)                                                        \
-  do {                                                                                         \
-    const char* sa_ = smem + (buf) * STAGE;                                                    \
-    const char* sw_ = sa_ + A_BYTES;                                                           \
-    const int h_ = lane >> 5;                                                                  \
-    const int c_ = Q ? 4 * ((kk) / 2) + 2 * h_ + ((kk) % 2) : (kk) * 2 + h_;                   \
-    _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                        \
-      const int r = wm * WTM + tm * 32 + (lane & 31);                                          \
-      F##b[tm] = *reinterpret_cast<const bf16x8_t*>(sa_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
-    }                                                                                          \
-    if constexpr (!Q) {                                                                        \
-      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
-        const int r = nrow[tn] + (lane & 31);                                                  \
-        F##a[tn] = *reinterpret_cast<const bf16x8_t*>(sw_ + r * ROWW + ((c_ ^ swz<CPW>(r)) << 4)); \
-      }                                                                                        \
-    } else if ((kk) == 0) {                                                                    \
-      const int qb_ = (kt0 + (ktv)) * BK / args.qblock;                                        \
-      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
-        const int r = nrow[tn] + (lane & 31);                                                  \
-        qsc[tn] = scl[r * sst + qb_];                                                          \
-        _Pragma("unroll") for (int pr = 0; pr < 2; ++pr) {                                     \
-          const u32x4_t v_ = *reinterpret_cast<const u32x4_t*>(                                \
-              sw_ + r * ROWW + (((2 * pr + h_) ^ swz<CPW>(r)) << 4));                          \
-          qraw[pr][tn][0] = v_[0];                                                             \
-          qraw[pr][tn][1] = v_[1];                                                             \
-          qraw[pr][tn][2] = v_[2];                                                             \
-          qraw[pr][tn][3] = v_[3];                                                             \
-        }                                                                                      \
-      }                                                                                        \
-    }                                                                                          \
-  } while (0)
-  // fp8 weights: widen the codes of sub-step kk into F##a
-#define MOE_WIDEN(F, kk)                                                                       \
-  do {                                                                                         \
-    if constexpr (Q) {                                                                         \
-      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                        \
-          F##a[tn] = fp8x8_to_bf16(qraw[(kk) / 2][tn][2 * ((kk) % 2)],                         \
-                                   qraw[(kk) / 2][tn][2 * ((kk) % 2) + 1], qsc[tn]);           \
-    }                                                                                          \
-  } while (0)
-
-  constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
-  static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
-  static_assert(NS == 2, "two-stage ring");
-  // Matrix ops of a stage's last sub-step issued ahead of the stage
-  // boundary: a quarter of them in the bf16 gate/up product with 256-row
-  // tiles (measured 3-4 % faster there); elsewhere none (equal or slower).
-  constexpr int PRE = (Q || MODE != kGateUpSilu || BM != 256) ? 0 : TM * TN / 4;
-
-  // matrix ops [first, first + count) of one sub-step (op i: weight sub-tile
-  // i / TM, token sub-tile i % TM)
-#define MOE_MMA(F, first, count)                                                               \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < TM * TN; ++i_) {                                   \
-      if (i_ >= (first) && i_ < (first) + (count)) {                                           \
-        const int tn_ = i_ / TM, tm_ = i_ % TM;                                                \
-        acc[tn_][tm_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[tn_], F##b[tm_],         \
-                                                                acc[tn_][tm_], 0, 0, 0);       \
-      }                                                                                        \
-    }                                                                                          \
-  } while (0)
-  // sub-steps 0 .. KK-2 of stage kt: the fragments of the next sub-step are
-  // read (and fp8 codes widened) around this sub-step's matrix ops
-#define MOE_SUBSTEPS(buf, kt)                                                                  \
-  do {                                                                                         \
-    _Pragma("unroll") for (int kk = 0; kk + 1 < KK; ++kk) {                                    \
-      if (kk % 2 == 0) {                                                                       \
-        MOE_LOAD_FRAGS(f1, buf, kk + 1, kt);                                                   \
-        MOE_MMA(f0, 0, TM * TN);                                                               \
-        MOE_WIDEN(f1, kk + 1);                                                                 \
-      } else {                                                                                 \
-        MOE_LOAD_FRAGS(f0, buf, kk + 1, kt);                                                   \
-        MOE_MMA(f1, 0, TM * TN);                                                               \
-        MOE_WIDEN(f0, kk + 1);                                                                 \
-      }                                                                                        \
-    }                                                                                          \
-  } while (0)
-
-  // prologue: stages 0 and 1 in flight (one per buffer; a missing stage 1
-  // reads out of range), stage 0 landed, its first fragments read
-  MOE_ISSUE_STAGE(0, 0);
-  MOE_ISSUE_STAGE(1, 1);
-  wait_vmcnt<LA + LB>();
-  __syncthreads();
-  bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
-  MOE_LOAD_FRAGS(f0, 0, 0, 0);
-  MOE_WIDEN(f0, 0);
-
-  // Every stage but the last. Its last sub-step's fragments are already in
-  // registers, so the stage boundary is interleaved with that sub-step's
-  // matrix ops: the first PRE of them, then the wait (stage kt+1 landed: it
-  // is the only stage in flight) and the barrier (every wave is done reading
-  // stage kt), then the loads of stage kt+2 into the buffer stage kt leaves
-  // (issued first: they have the longest way to go), the reads of stage
-  // kt+1's first fragments, then the rest of the matrix ops. The last stage
-  // is peeled off, so the loop body has no branch (with one, the
-  // accumulators are copied between register files around it).
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int buf = kt & 1;
-    MOE_SUBSTEPS(buf, kt);
-    MOE_MMA(f1, 0, PRE);
-    wait_vmcnt<0>();
     __syncthreads();
-    MOE_ISSUE_STAGE(buf, kt + 2);
-    MOE_LOAD_FRAGS(f0, buf ^ 1, 0, kt + 1);
-    MOE_MMA(f1, PRE, TM * TN - PRE);
+
+    // XCD-aware tile order. Logical tiles are ordered in groups of GM row
+    // tiles that sweep the weight tiles. Consecutive workgroup ids are dealt
+    // round-robin to the 8 XCDs, so the workgroup in slot s of XCD x takes
+    // tile w*8S + x*S + s%S of window w = s/S, S being the workgroups one XCD
+    // holds at once: the XCDs work through the same window of 8S tiles
+    // together (one expert's weights and token rows, which the last-level
+    // cache then serves to all of them), each on a contiguous run of S tiles
+    // that share rows in its own L2. The last, partial window is shared out
+    // evenly over the XCDs.
+    const int n_tiles = args.n_tiles;
+    const int per_split = args.max_tiles * n_tiles;
+    const int total = per_split * args.ksplit;
+    const int S = args.xcd_slots;
+    const int slot = vb / 8;
+    const int nfull = total / (8 * S);
+    const int pid = slot < nfull * S
+                        ? (slot / S) * 8 * S + (vb % 8) * S + slot % S
+                        : nfull * 8 * S + (vb % 8) * ((total - nfull * 8 * S + 7) / 8) +
+                              (slot - nfull * S);
+    if (pid >= total) continue;
+    const int split = pid / per_split;  // the contraction split is the slowest index
+    const int tpid = pid - split * per_split;
+    const int group = tpid / (args.group_m * n_tiles);
+    const int first_m = group * args.group_m;
+    const int gsize = min(args.max_tiles - first_m, args.group_m);
+    const int within = tpid - group * args.group_m * n_tiles;
+    const int mt = first_m + within % gsize;
+    const int ntile = within / gsize;
+    if (mt >= args.num_tiles[0]) continue;
+    const int e = args.tile_expert[mt];
+    const int64_t m0 = (int64_t)mt * BM;
+    const int64_t kdim = args.kdim;
+
+    // weight row (within the expert) of staged row n of this tile, or -1
+    auto weight_row = [&](int n) -> int64_t {
+      if (MODE == kGateUpSilu) {
+        const int64_t n0g = (int64_t)ntile * (BN / 2);
+        return n < BN / 2 ? n0g + n : args.inter + n0g + (n - BN / 2);
+      }
+      const int64_t row = (int64_t)ntile * BN + n;
+      return row < args.n_out ? row : -1;
+    };
+
+    // ---- per-lane load offsets (fixed over the K loop) ----
+    // load j of this wave covers staged rows RPL*g .. RPL*g+RPL-1 (g = wave*L
+    // + j); lane -> row RPL*g + lane/CPR, physical chunk lane%CPR, logical
+    // chunk (lane%CPR) ^ swz(row): the XOR layout is applied on the global side.
+    uint32_t aoff[LA], boff[LB];
+    const uint16_t* a_base = MODE == kGateUpSilu ? args.a : args.a + m0 * kdim;
+    const uint32_t a_num = MODE == kGateUpSilu ? args.a_bytes : (uint32_t)(BM * kdim * 2);
+    const char* b_base =
+        Q ? reinterpret_cast<const char*>(args.wq) + (int64_t)e * args.w_expert_stride
+          : reinterpret_cast<const char*>(args.w + (int64_t)e * args.w_expert_stride);
+    const uint32_t b_num = (uint32_t)(args.w_expert_stride * (Q ? 1 : 2));
+    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a_base, a_num);
+    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(b_base, b_num);
+    // token rows of the tile's slots: every lookup issued before the first
+    // use, offsets computed without branches
+    int32_t fsl[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      fsl[j] = MODE == kGateUpSilu ? args.sorted[m0 + RPL * (wave * LA + j) + lane / CPR] : 0;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+      const int r = RPL * (wave * LA + j) + lane / CPR;
+      const uint32_t cb = (uint32_t)(((lane % CPR) ^ swz<CPR>(r)) * 16);
+      if (MODE == kGateUpSilu) {
+        const int32_t f = fsl[j];
+        const uint32_t t = (uint32_t)(f >= 0 ? f : 0) / (uint32_t)args.topk;
+        aoff[j] = f >= 0 ? t * (uint32_t)(kdim * 2) + cb : kOutOfRange;
+      } else {
+        aoff[j] = (uint32_t)(r * kdim * 2) + cb;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+      const int n = RPW * (wave * LB + j) + lane / CPW;
+      const uint32_t cb = (uint32_t)(((lane % CPW) ^ swz<CPW>(n)) * 16);
+      const int64_t row = weight_row(n);
+      boff[j] = row >= 0 ? (uint32_t)(row * kdim * (Q ? 1 : 2)) + cb : kOutOfRange;
+    }
+
+    // fp8 weights: the tile's scales go to LDS ahead of stage 0's loads (and
+    // so have landed once stage 0 has: loads complete in issue order)
+    int sst = 1;
+    if constexpr (Q) {
+      const int nqb = args.nqb;
+      sst = nqb | 1;
+      const int64_t rows_pe = args.w_expert_stride / kdim;
+      const __amdgpu_buffer_rsrc_t rsrc_s =
+          make_rsrc(args.wscale + (int64_t)e * rows_pe * nqb, (uint32_t)(rows_pe * nqb * 4));
+      for (int p0 = wave * 64; p0 < BN * sst; p0 += NW * 64) {
+        const int p = p0 + lane;
+        const int n = p / sst, b = p - n * sst;
+        const int64_t row = n < BN ? weight_row(n) : -1;
+        const uint32_t off = (row >= 0 && b < nqb) ? (uint32_t)((row * nqb + b) * 4) : kOutOfRange;
+        load_lds_b32(rsrc_s, reinterpret_cast<const char*>(scl) + p0 * 4, off);
+      }
+    }
+
+    // LDS row of each of this wave's weight sub-tiles
+    int nrow[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      if (MODE == kGateUpSilu) {
+        nrow[tn] = tn < TN / 2 ? wn * (WTN / 2) + tn * 32
+                               : BN / 2 + wn * (WTN / 2) + (tn - TN / 2) * 32;
+      } else {
+        nrow[tn] = wn * WTN + tn * 32;
+      }
+    }
+
+    f32x16_t acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    const int nk = (int)(kdim / BK) / args.ksplit;  // stages of this split
+    const int kt0 = split * nk;                     // its first stage
+
+    // Loads of stage kt into LDS buffer `buf`; stages past the last one read
+    // out of range (nothing is fetched, the buffer, which is not read again,
+    // receives zeros), so the issue needs no branch.
+#define MOE_ISSUE_STAGE(buf, kt)                                                              \
+    do {                                                                                        \
+      const bool live_ = (kt) < nk;                                                             \
+      const uint32_t sa_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWB : kOutOfRange;                 \
+      const uint32_t sw_ = live_ ? (uint32_t)(kt0 + (kt)) * ROWW : kOutOfRange;                 \
+      const char* sb_ = smem + (buf) * STAGE;                                                   \
+      _Pragma("unroll") for (int j = 0; j < LA; ++j)                                           \
+          load_lds_b128(rsrc_a, sb_ + (wave * LA + j) * 1024, aoff[j], sa_);                    \
+      _Pragma("unroll") for (int j = 0; j < LB; ++j)                                           \
+          load_lds_b128(rsrc_b, sb_ + A_BYTES + (wave * LB + j) * 1024, boff[j], sw_);          \
+    } while (0)
+
+    // Fragment reads of sub-step kk of stage kt (in LDS buffer `buf`); the
+    // lane holds 8 k values of its row. bf16 weights: chunk 2*kk + lane/32 of
+    // both 128-byte rows. fp8 weights: one 16-byte chunk of a 64-byte weight
+    // row holds 8 codes for each of two sub-steps, so sub-steps 2j and 2j+1
+    // take the two halves of chunk 2j + lane/32, and the token fragment reads
+    // the matching k values (a fixed permutation of k inside the stage, the
+    // same on both operands). Both chunks of a stage are read with its first
+    // sub-step; each sub-step's codes are widened, as bf16(fp32(code) * scale),
+    // after the matrix ops of the sub-step before it have been issued, so the
+    // conversion overlaps them.
+    uint32_t qraw[Q ? 2 : 1][Q ? TN : 1][4];
+    float qsc[Q ? TN : 1];
+#define MOE_LOAD_FRAGS(F, buf, kk, ktv)                                                        \
+    do {                                                                                         \
+      const char* sa_ = smem + (buf) * STAGE;                                                    \
+      const char* sw_ = sa_ + A_BYTES;                                                           \
+      const int h_ = lane >> 5;                                                                  \
+      const int c_ = Q ? 4 * ((kk) / 2) + 2 * h_ + ((kk) % 2) : (kk) * 2 + h_;                   \
+      _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                        \
+        const int r = wm * WTM + tm * 32 + (lane & 31);                                          \
+        F##b[tm] = *reinterpret_cast<const bf16x8_t*>(sa_ + r * ROWB + ((c_ ^ swz<CPR>(r)) << 4)); \
+      }                                                                                          \
+      if constexpr (!Q) {                                                                        \
+        _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
+          const int r = nrow[tn] + (lane & 31);                                                  \
+          F##a[tn] =                                                                           \
+              *reinterpret_cast<const bf16x8_t*>(sw_ + r * ROWW + ((c_ ^ swz<CPW>(r)) << 4));  \
+        }                                                                                        \
+      } else if ((kk) == 0) {                                                                    \
+        const int qb_ = (kt0 + (ktv)) * BK / args.qblock;                                        \
+        _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                      \
+          const int r = nrow[tn] + (lane & 31);                                                  \
+          qsc[tn] = scl[r * sst + qb_];                                                          \
+          _Pragma("unroll") for (int pr = 0; pr < 2; ++pr) {                                     \
+            const u32x4_t v_ = *reinterpret_cast<const u32x4_t*>(                                \
+                sw_ + r * ROWW + (((2 * pr + h_) ^ swz<CPW>(r)) << 4));                          \
+            qraw[pr][tn][0] = v_[0];                                                             \
+            qraw[pr][tn][1] = v_[1];                                                             \
+            qraw[pr][tn][2] = v_[2];                                                             \
+            qraw[pr][tn][3] = v_[3];                                                             \
+          }                                                                                      \
+        }                                                                                        \
+      }                                                                                          \
+    } while (0)
+    // fp8 weights: widen the codes of sub-step kk into F##a
+#define MOE_WIDEN(F, kk)                                                                       \
+    do {                                                                                         \
+      if constexpr (Q) {                                                                         \
+        _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                        \
+            F##a[tn] = fp8x8_to_bf16(qraw[(kk) / 2][tn][2 * ((kk) % 2)],                         \
+                                     qraw[(kk) / 2][tn][2 * ((kk) % 2) + 1], qsc[tn]);           \
+      }                                                                                          \
+    } while (0)
+
+    constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
+    static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
+    static_assert(NS == 2, "two-stage ring");
+    // Matrix ops of a stage's last sub-step issued ahead of the stage
+    // boundary: a quarter of them in the bf16 gate/up product with 256-row
+    // tiles (measured 3-4 % faster there); elsewhere none (equal or slower).
+    constexpr int PRE = (Q || MODE != kGateUpSilu || BM != 256) ? 0 : TM * TN / 4;
+
+    // matrix ops [first, first + count) of one sub-step (op i: weight sub-tile
+    // i / TM, token sub-tile i % TM)
+#define MOE_MMA(F, first, count)                                                               \
+    do {                                                                                         \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM * TN; ++i_) {                                   \
+        if (i_ >= (first) && i_ < (first) + (count)) {                                           \
+          const int tn_ = i_ / TM, tm_ = i_ % TM;                                                \
+          acc[tn_][tm_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[tn_], F##b[tm_],         \
+                                                                  acc[tn_][tm_], 0, 0, 0);       \
+        }                                                                                        \
+      }                                                                                          \
+    } while (0)
+    // sub-steps 0 .. KK-2 of stage kt: the fragments of the next sub-step are
+    // read (and fp8 codes widened) around this sub-step's matrix ops
+#define MOE_SUBSTEPS(buf, kt)                                                                  \
+    do {                                                                                         \
+      _Pragma("unroll") for (int kk = 0; kk + 1 < KK; ++kk) {                                    \
+        if (kk % 2 == 0) {                                                                       \
+          MOE_LOAD_FRAGS(f1, buf, kk + 1, kt);                                                   \
+          MOE_MMA(f0, 0, TM * TN);                                                               \
+          MOE_WIDEN(f1, kk + 1);                                                                 \
+        } else {                                                                                 \
+          MOE_LOAD_FRAGS(f0, buf, kk + 1, kt);                                                   \
+          MOE_MMA(f1, 0, TM * TN);                                                               \
+          MOE_WIDEN(f0, kk + 1);                                                                 \
+        }                                                                                        \
+      }                                                                                          \
+    } while (0)
+
+    // prologue: stages 0 and 1 in flight (one per buffer; a missing stage 1
+    // reads out of range), stage 0 landed, its first fragments read
+    MOE_ISSUE_STAGE(0, 0);
+    MOE_ISSUE_STAGE(1, 1);
+    wait_vmcnt<LA + LB>();
+    __syncthreads();
+    bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
+    MOE_LOAD_FRAGS(f0, 0, 0, 0);
     MOE_WIDEN(f0, 0);
-  }
-  MOE_SUBSTEPS((nk - 1) & 1, nk - 1);
-  MOE_MMA(f1, 0, TM * TN);
+
+    // Every stage but the last. Its last sub-step's fragments are already in
+    // registers, so the stage boundary is interleaved with that sub-step's
+    // matrix ops: the first PRE of them, then the wait (stage kt+1 landed: it
+    // is the only stage in flight) and the barrier (every wave is done reading
+    // stage kt), then the loads of stage kt+2 into the buffer stage kt leaves
+    // (issued first: they have the longest way to go), the reads of stage
+    // kt+1's first fragments, then the rest of the matrix ops. The last stage
+    // is peeled off, so the loop body has no branch (with one, the
+    // accumulators are copied between register files around it).
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const int buf = kt & 1;
+      MOE_SUBSTEPS(buf, kt);
+      MOE_MMA(f1, 0, PRE);
+      wait_vmcnt<0>();
+      __syncthreads();
+      MOE_ISSUE_STAGE(buf, kt + 2);
+      MOE_LOAD_FRAGS(f0, buf ^ 1, 0, kt + 1);
+      MOE_MMA(f1, PRE, TM * TN - PRE);
+      MOE_WIDEN(f0, 0);
+    }
+    MOE_SUBSTEPS((nk - 1) & 1, nk - 1);
+    MOE_MMA(f1, 0, TM * TN);
 #undef MOE_SUBSTEPS
 #undef MOE_MMA
 #undef MOE_WIDEN
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
-  tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane, split);
+    tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane, split);
   }  // persistent tile loop
 }
 
