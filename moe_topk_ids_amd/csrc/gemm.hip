@@ -606,6 +606,7 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   // (token rows, weight rows, waves): the variants kept after sweeping tile
   // shape, pipeline depth and wave layout on the workloads' shapes
   if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE, Q>(a, stream);
+  if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
   if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
   if (cfg.bm == 192 && cfg.bn == 256) return launch_cfg<192, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
@@ -633,7 +634,12 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
 // prefill shape) takes 1.15: with it the model picks 192x256 where it
 // measured fastest (T=4195 and T=4098 with E=8, T=2400 with E=128: 12-19 %
 // less than the previous pick) and keeps 256x256 where that stays ahead
-// (T >= 8192 with E=128, the large E=8 shapes).
+// (T >= 8192 with E=128, the large E=8 shapes). 64x128 gate/up tiles (three
+// workgroups per CU; the down projection keeps 64x256) take 0.925 (between
+// the 0.91 that T=520 and T=668 need and the 0.938 that keeps 128x128 at
+// T=277, where it measured 14 % faster) and are a
+// candidate only while they fit one round: picked at T=135 and T=668 with
+// E=8 (80 -> 73 and 107 -> 100 us per call) and T=520 with E=128 (-2 %).
 namespace {
 double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
   const int64_t n = T * K;
@@ -652,26 +658,39 @@ double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
   return live * acc / wsum;
 }
 
+double tile_eff(GemmCfg c) {
+  if (c.bm == 64) return c.bn == 128 ? 0.925 : 0.91;
+  return c.bm == 128 ? 1.0 : c.bm == 192 ? 1.15 : 1.23;
+}
+
+// c: the gate/up tile; the down projection runs pick_gemm2_cfg's tile on the
+// same row layout.
 double model_cost(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E, GemmCfg c) {
-  const double eff = c.bm == 64 ? 0.91 : c.bm == 128 ? 1.0 : c.bm == 192 ? 1.15 : 1.23;
   const double rt = expected_row_tiles(T, K, E, c.bm);
-  const double prod[2][2] = {{(double)H, (double)(2 * I / c.bn)},                  // gate/up
-                             {(double)I, (double)((H + c.bn - 1) / c.bn)}};  // down
+  const GemmCfg c2 = pick_gemm2_cfg(T * K, H, I, E, c.bm);
+  const GemmCfg cg[2] = {c, c2};
+  const double prod[2][2] = {{(double)H, (double)(2 * I / c.bn)},                   // gate/up
+                             {(double)I, (double)((H + c2.bn - 1) / c2.bn)}};  // down
   double t = 0.0;
   for (int g = 0; g < 2; ++g) {
     const double per_cu = rt * prod[g][1] / 256.0;
-    const double rounds = c.bm >= 192 ? fmax(1.0, ceil(per_cu - 0.02)) : fmax(1.0, per_cu);
-    t += rounds * (double)c.bm * c.bn * prod[g][0] * 2.0 / eff;
+    const double rounds = cg[g].bm >= 192 ? fmax(1.0, ceil(per_cu - 0.02)) : fmax(1.0, per_cu);
+    t += rounds * (double)cg[g].bm * cg[g].bn * prod[g][0] * 2.0 / tile_eff(cg[g]);
   }
   return t;
 }
 }  // namespace
 
 GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
-  const GemmCfg cands[4] = {{64, 256}, {128, 128}, {192, 256}, {256, 256}};
-  GemmCfg best = cands[1];
+  const GemmCfg cands[5] = {{64, 128}, {64, 256}, {128, 128}, {192, 256}, {256, 256}};
+  GemmCfg best = cands[2];
   double best_t = model_cost(T, K, H, I, E, best);
   for (const GemmCfg& c : cands) {
+    // 64x128 gate/up tiles (three workgroups per CU) only while all of them
+    // fit one round of the chip: beyond it they measured 6-14 % slower than
+    // 64x256 (E=128: T=1019, 2044; T=4195 with I=768)
+    if (c.bn == 128 && c.bm == 64 && expected_row_tiles(T, K, E, 64) * (2 * I / 128) > 3 * 256)
+      continue;
     const double t = model_cost(T, K, H, I, E, c);
     if (t < best_t) {
       best = c;

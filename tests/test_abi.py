@@ -147,7 +147,10 @@ def test_workspace_and_tile_queries(lib):
 
 def test_tile_choice(lib):
     # the cost model's picks on shapes where the measured winner is clear
-    assert moe.moe_m_tile(135, 2048, 2048, 8, 2) == 128    # few rows: more tiles in flight
+    # ~34 rows per expert: 64-row tiles, 64x128 for the gate/up product (three
+    # workgroups per CU, all tiles in one round)
+    assert moe.moe_m_tile(135, 2048, 2048, 8, 2) == 64
+    assert moe.moe_m_tile(277, 2048, 2048, 8, 2) == 128    # ~69 rows: one 128-row tile each
     assert moe.moe_m_tile(668, 2048, 2048, 8, 2) == 64     # ~167 rows per expert: least padding
     assert moe.moe_m_tile(8192, 4096, 384, 128, 8) == 256  # many tiles: the big tile's efficiency
     assert moe.moe_m_tile(15381, 4096, 4096, 8, 2) == 256
