@@ -621,25 +621,26 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
 // row count is binomial (mean T*K/E, variance T*(K/E)*(1-K/E)); the expected
 // number of BM-row tiles it needs is averaged over five points of the
 // normal approximation. A product's time is then taken as (tiles per CU) x
-// (flops per tile) / (relative tile efficiency). 64x256 and 128x128 tiles
-// run two workgroups per CU, so their tail rounds overlap and the count
-// stays fractional; 192x256 and 256x256 tiles fill a CU alone, so they are
-// rounded up to whole rounds. The efficiencies (64x256 0.91, 128x128 1,
-// 256x256 1.23) were fitted to measured times of those three
-// configurations on every shape of the atrex-bench shapes table; against
-// the fastest configuration per shape the model gives up at most 1-2 %
-// except in the weight-streaming corner (E=128, I=384, ~32 rows per
-// expert), where 128x128 is 10 % faster. 192x256 (0.9 the padding of
+// (flops per tile) / (relative tile efficiency). Tiles that share a CU
+// (64x128 three to a CU, 64x256 and 128x128 two) overlap their tail rounds,
+// so the count stays fractional; 192x256 and 256x256 tiles fill a CU alone,
+// so they are rounded up to whole rounds. The down-projection term uses the
+// tile that product runs (64x256 on the 64-row layout).
+//
+// The efficiencies (64x256 0.91, 128x128 1, 256x256 1.23) were fitted to
+// measured times of those three configurations on every shape of the
+// atrex-bench shapes table; against the fastest configuration per shape the
+// model gives up at most 1-2 %, except at T=4195 with E=128, I=768, where
+// 128x128 is 3 % faster than its 64x256. 192x256 (0.9 the padding of
 // 256-row tiles on ~1050-row experts, and exactly three rounds for the
 // prefill shape) takes 1.15: with it the model picks 192x256 where it
 // measured fastest (T=4195 and T=4098 with E=8, T=2400 with E=128: 12-19 %
 // less than the previous pick) and keeps 256x256 where that stays ahead
-// (T >= 8192 with E=128, the large E=8 shapes). 64x128 gate/up tiles (three
-// workgroups per CU; the down projection keeps 64x256) take 0.925 (between
-// the 0.91 that T=520 and T=668 need and the 0.938 that keeps 128x128 at
-// T=277, where it measured 14 % faster) and are a
+// (T >= 8192 with E=128, the large E=8 shapes). 64x128 gate/up tiles take
+// 0.925, between the 0.91 that T=520 and T=668 need and the 0.938 above
+// which they would displace 128x128 at T=277 (14 % faster there), and are a
 // candidate only while they fit one round: picked at T=135 and T=668 with
-// E=8 (80 -> 73 and 107 -> 100 us per call) and T=520 with E=128 (-2 %).
+// E=8 (81 -> 76 and 111 -> 105-110 us per call) and T=520 with E=128 (-2 %).
 namespace {
 double expected_row_tiles(int64_t T, int64_t K, int64_t E, int bm) {
   const int64_t n = T * K;
