@@ -96,9 +96,10 @@ extern "C" {
  * size allocates and is therefore not graph-capture safe. Calls that use the
  * internal workspace of one device share it: they must be ordered (one
  * stream, or synchronised), else give each concurrent caller its own
- * workspace through moe_forward_ex. The combine mode
- * comes from the environment variable MOE_COMBINE ("slot", the default, or
- * "atomic"), read once.
+ * workspace through moe_forward_ex. Two environment variables, read once
+ * per process, set its flags: MOE_COMBINE ("slot", the default, or "atomic":
+ * MOE_FLAG_ATOMIC_COMBINE) and MOE_DEBUG_SYNC (any value but "" or "0":
+ * MOE_FLAG_DEBUG_SYNC).
  */
 int moe_forward(const void* hidden, const void* w1, const void* w2,
                 const float* topk_weights, const int32_t* topk_ids,
@@ -220,7 +221,11 @@ size_t moe_route_scratch_bytes(int64_t T, int64_t K, int64_t E);
  * [capacity, I] (row-major); rows >= offsets[E] are not written.
  * `max_tiles` = capacity / m_tile bounds the launch. m_tile must be 64, 128,
  * 192 or 256 (the row tiles the grouped GEMMs are built for; moe_m_tile
- * returns one of them).
+ * returns one of them). sorted, tile_expert and num_tiles must come from
+ * moe_route called with the same E and m_tile (and these T, K); a tile whose
+ * expert is outside [0, E) is skipped, never read past w1. When m_tile equals
+ * moe_m_tile(T, H, I, E, K, 0) this runs exactly the gate/up kernel (tile
+ * width included) that moe_forward runs for these sizes.
  */
 int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
                    const int32_t* tile_expert, const int32_t* num_tiles,

@@ -301,8 +301,18 @@ def moe_route(topk_ids, E, m_tile, stream=None) -> dict:
                          _ptr(r["sorted"]), _ptr(r["slot_of"]), _ptr(r["tile_expert"]),
                          _ptr(r["num_tiles"]), cap, _ptr(scratch), _stream(stream)))
     r["capacity"] = cap
+    r["E"], r["K"], r["m_tile"], r["T"] = E, K, m_tile, T
     r["_scratch"] = scratch  # keep alive until the stream passes the work
     return r
+
+
+def _check_route(route: dict, T: int, E: int, K: int, m_tile: int):
+    """The routing arrays must come from moe_route for these sizes: the
+    GEMMs index w1 by the tile experts and read ``capacity`` rows."""
+    got = (route.get("T"), route.get("E"), route.get("K"), route.get("m_tile"))
+    if got != (T, E, K, m_tile):
+        raise ValueError(f"route was built for (T, E, K, m_tile) = {got}, this call needs "
+                         f"{(T, E, K, m_tile)}")
 
 
 def moe_gemm1_silu(hidden_states, w1, route: dict, K: int, m_tile: int, act=None, stream=None):
@@ -316,6 +326,7 @@ def moe_gemm1_silu(hidden_states, w1, route: dict, K: int, m_tile: int, act=None
     T, H = hidden_states.shape
     E, I2, _ = w1.shape
     I = I2 // 2
+    _check_route(route, T, E, K, m_tile)
     cap = route["capacity"]
     if act is None:
         act = torch.zeros((max(cap, 1), I), dtype=torch.bfloat16, device=hidden_states.device)
@@ -344,6 +355,7 @@ def moe_gemm1_silu_fp8(hidden_states, w1q, w1_scale, block: int, route: dict, K:
     I = I2 // 2
     if tuple(w1q.shape) != (E, 2 * I, H) or tuple(w1_scale.shape) != (E, 2 * I, H // block):
         raise ValueError("w1q must be [E,2I,H] and w1_scale [E,2I,H/block]")
+    _check_route(route, T, E, K, m_tile)
     cap = route["capacity"]
     if act is None:
         act = torch.zeros((max(cap, 1), I), dtype=torch.bfloat16, device=hidden_states.device)

@@ -14,6 +14,7 @@
 //                  activation rows, and writes
 //                  out[t, h] = sum_k w_k * (w2[e_k, h, :] . act[t*K+k, :]).
 // No atomics: each output element is produced by exactly one wave.
+#include "device_util.h"
 #include "moe_internal.h"
 
 
@@ -23,12 +24,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDownIter = 32;  // 16-byte chunks per lane held in registers
-
-__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
 
 __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
   float s = bf16lo(a[0]) * bf16lo(b[0]);
@@ -43,24 +38,6 @@ __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
 }
 __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   return dot8(u32x4_t{a.x, a.y, a.z, a.w}, u32x4_t{b.x, b.y, b.z, b.w});
-}
-
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
-                                            false);
-  return v + __builtin_bit_cast(float, m);
-}
-
-// Sum over the wave with DPP moves (no LDS round trips); the total ends up
-// in lane 63.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]
-  v = dpp_add<0x141>(v);       // row_half_mirror
-  v = dpp_add<0x140>(v);       // row_mirror: every lane holds its row's sum
-  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  return dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
 }
 
 // One wave per (slot, IPW consecutive intermediate columns): the IPW gate
@@ -83,10 +60,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup(
   const int64_t t = f / K;
   const int64_t nc = H / 8;
   // buffer loads: offsets past the end read zeros (no branches, no scratch)
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(hidden + t * H), (short)0, (int)(H * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(w1 + (int64_t)e * 2 * I * H), (short)0, (int)(2 * I * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(hidden + t * H, (uint32_t)(H * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w1 + (int64_t)e * 2 * I * H, (uint32_t)(2 * I * H * 2));
   u32x4_t wv[2 * IPW][NC], xv[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {

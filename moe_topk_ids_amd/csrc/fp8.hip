@@ -19,6 +19,7 @@
 // then runs the bf16 MFMA GEMMs unchanged.
 #include <algorithm>
 
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -27,14 +28,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBitmapWords = kMaxExperts / 32;
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 // 16 fp8 codes (one 16-byte chunk) times 16 bf16 values (two chunks), fp32.
 __device__ __forceinline__ float dot16(u32x4_t q, u32x4_t xa, u32x4_t xb) {
@@ -64,11 +58,6 @@ __device__ __forceinline__ void fp8x4_to_bf16(uint32_t qw, uint32_t& p0, uint32_
   p1 = (__float_as_uint(h0) >> 16) | (__float_as_uint(h1) & 0xffff0000u);
 }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
-}
-
 // 16 bf16 weights (8 packed pairs) times 16 bf16 values (two chunks).
 __device__ __forceinline__ float dot16_bf16(const uint32_t (&w)[8], u32x4_t xa, u32x4_t xb) {
   const uint32_t a0 = xa[0], a1 = xa[1], a2 = xa[2], a3 = xa[3];
@@ -81,35 +70,6 @@ __device__ __forceinline__ float dot16_bf16(const uint32_t (&w)[8], u32x4_t xa, 
   s = dot2(w[5], b1, s);
   s = dot2(w[6], b2, s);
   return dot2(w[7], b3, s);
-}
-
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
-                                            false);
-  return v + __builtin_bit_cast(float, m);
-}
-
-// Sum over aligned groups of G lanes; the total ends up in the group's last
-// lane (DPP: quad_perm, half-row and row mirrors, row broadcasts).
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-  if (G >= 2) v = dpp_add<0xB1>(v);
-  if (G >= 4) v = dpp_add<0x4E>(v);
-  if (G >= 8) v = dpp_add<0x141>(v);
-  if (G >= 16) v = dpp_add<0x140>(v);
-  if (G >= 32) v = dpp_add<0x142, 0xA>(v);
-  if (G >= 64) v = dpp_add<0x143, 0xC>(v);
-  return v;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint16_t to_bf16_bits(float v) {
-  const __bf16 b = (__bf16)v;  // round to nearest even
-  return __builtin_bit_cast(uint16_t, b);
 }
 
 // ---- grouped path: widen to bf16 ----
@@ -186,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_q(QArgs a) {
   const int64_t t = f / a.K;
   const int64_t nc = H / 16, nb = H / a.block;
   const int64_t rg = (int64_t)e * 2 * I + i, ru = rg + I;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.w1q + (int64_t)e * 2 * I * H, 2 * I * H);
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.hidden + t * H, H * 2);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w1q + (int64_t)e * 2 * I * H, (uint32_t)(2 * I * H));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.hidden + t * H, (uint32_t)(H * 2));
   u32x4_t gq[NC], uq[NC], xa[NC], xb[NC];
   float sg[NC], su[NC];
 #pragma unroll
@@ -319,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void sb_gateup_q(QArgs a) {
   if (i >= I) return;
   const int64_t nc = H / 16, nb = H / a.block;
   const int64_t rg = (int64_t)e * 2 * I + i, ru = rg + I;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.w1q + (int64_t)e * 2 * I * H, 2 * I * H);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w1q + (int64_t)e * 2 * I * H, (uint32_t)(2 * I * H));
   uint32_t gw[NC][8], uw[NC][8];
   float sg[NC], su[NC];
 #pragma unroll
@@ -341,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void sb_gateup_q(QArgs a) {
   const int32_t count = s_count;
   for (int32_t m = 0; m < count; ++m) {
     const int32_t f = s_slots[m];
-    const __amdgpu_buffer_rsrc_t xr = rsrc(a.hidden + (int64_t)(f / a.K) * H, H * 2);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.hidden + (int64_t)(f / a.K) * H, (uint32_t)(H * 2));
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -382,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void sb_down_q(QArgs a) {
   const bool h_ok = h < H;
   const int64_t cpr = I / 16, nb = I / a.block;
   const int64_t row = (int64_t)e * H + (h_ok ? h : 0);
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.w2q + (int64_t)e * H * I, H * I);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w2q + (int64_t)e * H * I, (uint32_t)(H * I));
   uint32_t ww[JD][8];
   float sc[JD];
 #pragma unroll
@@ -400,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void sb_down_q(QArgs a) {
   const int32_t count = s_count;
   for (int32_t m = 0; m < count; ++m) {
     const int32_t f = s_slots[m];
-    const __amdgpu_buffer_rsrc_t ar = rsrc(a.act + (int64_t)f * I, I * 2);
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.act + (int64_t)f * I, (uint32_t)(I * 2));
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < JD; ++j) {

@@ -38,6 +38,7 @@
 // kernel does when it fetches matching w1 and w3 blocks of one expert.
 #include <algorithm>
 
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -46,7 +47,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 
@@ -66,6 +66,7 @@ struct GemmArgs {
   int64_t inter;            // I (GEMM1: offset of the up rows)
   uint32_t a_bytes;         // bytes of the token operand (GEMM1 gather bound)
   int32_t topk;             // K
+  int32_t n_experts;        // E (a tile whose expert is outside [0, E) is skipped)
   int32_t max_tiles;        // row tiles the grid was sized for
   int32_t n_tiles;          // weight-row tiles
   int32_t group_m;          // row tiles per scheduling group
@@ -105,16 +106,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Buffer resource for raw (unstructured) loads: bytes past num_records read
-// as zero, which is how pad rows and out-of-range weight rows are zero-filled
-// without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
-                                                            uint32_t num_records) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records,
-                                           0x00020000);
-}
-
-constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= num_records reads zeros
+// Pad rows and out-of-range weight rows are read through make_rsrc's
+// out-of-range offset (kOutOfRange): they arrive as zeros without branches.
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -338,6 +331,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     const int ntile = within / gsize;
     if (mt >= args.num_tiles[0]) continue;
     const int e = args.tile_expert[mt];
+    if ((uint32_t)e >= (uint32_t)args.n_experts) continue;
     const int64_t m0 = (int64_t)mt * BM;
     const int64_t kdim = args.kdim;
 
@@ -734,9 +728,10 @@ GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm)
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
-                             int64_t K, int64_t max_tiles, uint16_t* act, const Epilogue& ep,
-                             hipStream_t stream) {
+                             int64_t E, int64_t K, int64_t max_tiles, uint16_t* act,
+                             const Epilogue& ep, hipStream_t stream) {
   GemmArgs a{};
+  a.n_experts = (int32_t)E;
   a.ksplit = 1;
   a.act = ep.act;
   a.alpha = ep.alpha;
@@ -762,10 +757,12 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
-                        int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
-                        const float* b2, hipStream_t stream, int ksplit, int64_t n_slots) {
+                        int64_t I, int64_t E, int64_t K, int64_t max_tiles, float* y,
+                        float* out, const float* b2, hipStream_t stream, int ksplit,
+                        int64_t n_slots) {
   if (out && ksplit > 1) return hipErrorInvalidValue;  // atomic adds of partial sums
   GemmArgs a{};
+  a.n_experts = (int32_t)E;
   a.ksplit = ksplit;
   a.part_stride = n_slots * H;
   a.bias = out ? b2 : nullptr;  // on the slot path the combine adds b2
@@ -794,10 +791,11 @@ bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block) {
 hipError_t launch_gemm1_silu_fp8(GemmCfg cfg, const uint16_t* hidden, const uint8_t* w1q,
                                  const float* w1s, int64_t block, const int32_t* sorted,
                                  const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
-                                 int64_t H, int64_t I, int64_t K, int64_t max_tiles,
+                                 int64_t H, int64_t I, int64_t E, int64_t K, int64_t max_tiles,
                                  uint16_t* act, const Epilogue& ep, hipStream_t stream) {
   if (!fp8_gemm_supported(H, I, block)) return hipErrorInvalidValue;
   GemmArgs a{};
+  a.n_experts = (int32_t)E;
   a.ksplit = 1;
   a.act = ep.act;
   a.alpha = ep.alpha;
@@ -826,12 +824,13 @@ hipError_t launch_gemm1_silu_fp8(GemmCfg cfg, const uint16_t* hidden, const uint
 hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q,
                             const float* w2s, int64_t block, const int32_t* sorted,
                             const int32_t* tile_expert, const int32_t* num_tiles,
-                            const float* topk_weights, int64_t H, int64_t I, int64_t K,
-                            int64_t max_tiles, float* y, float* out, const float* b2,
+                            const float* topk_weights, int64_t H, int64_t I, int64_t E,
+                            int64_t K, int64_t max_tiles, float* y, float* out, const float* b2,
                             hipStream_t stream, int ksplit, int64_t n_slots) {
   if (!fp8_gemm_supported(H, I, block)) return hipErrorInvalidValue;
   if (out && ksplit > 1) return hipErrorInvalidValue;
   GemmArgs a{};
+  a.n_experts = (int32_t)E;
   a.ksplit = ksplit;
   a.part_stride = n_slots * H;
   a.bias = out ? b2 : nullptr;  // on the slot path the combine adds b2

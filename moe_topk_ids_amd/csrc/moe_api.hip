@@ -154,6 +154,17 @@ int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fl
   return MOE_PATH_GROUPED;
 }
 
+// The gate/up tile the GEMM1 entry points run for routing arrays of row tile
+// m_tile: the forward's own tile when m_tile is the one the forward picks for
+// these sizes (so the entry point runs exactly the forward's kernel), else
+// the default width for that row tile.
+moe::GemmCfg gemm1_entry_cfg(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                             int32_t m_tile) {
+  const moe::GemmCfg fwd = moe::pick_gemm1_cfg(T, K, H, I, E);
+  if (fwd.bm == m_tile) return fwd;
+  return moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256};
+}
+
 bool use_decode(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   return pick_path(T, H, I, E, K, flags) == MOE_PATH_DECODE;
 }
@@ -256,10 +267,18 @@ int internal_workspace(size_t need, void** out) {
   return MOE_OK;
 }
 
+// Flags of plain moe_forward, read once from the environment: MOE_COMBINE
+// ("slot", the default, or "atomic") and MOE_DEBUG_SYNC (non-empty and not
+// "0": synchronise after every stage and name the failing one, as the
+// metrale forward_k2 dispatch does under its stage-diagnostics lever).
 uint32_t env_flags() {
   static uint32_t flags = [] {
+    uint32_t f = 0;
     const char* c = std::getenv("MOE_COMBINE");
-    return (c && std::strcmp(c, "atomic") == 0) ? MOE_FLAG_ATOMIC_COMBINE : 0u;
+    if (c && std::strcmp(c, "atomic") == 0) f |= MOE_FLAG_ATOMIC_COMBINE;
+    const char* d = std::getenv("MOE_DEBUG_SYNC");
+    if (d && d[0] != '\0' && std::strcmp(d, "0") != 0) f |= MOE_FLAG_DEBUG_SYNC;
+    return f;
   }();
   return flags;
 }
@@ -410,30 +429,30 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                       sorted, slot_of, tile_expert, num_tiles, stream);
     if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
     st = q_native ? moe::launch_gemm1_silu_fp8(L.g1, x, q->w1q, q->w1s, q->block, sorted,
-                                               tile_expert, num_tiles, T, H, I, K, L.max_tiles,
-                                               act, ep, stream)
+                                               tile_expert, num_tiles, T, H, I, E, K,
+                                               L.max_tiles, act, ep, stream)
                   : moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I,
-                                           K, L.max_tiles, act, ep, stream);
+                                           E, K, L.max_tiles, act, ep, stream);
     if ((rc = stage_check(flags, "gemm1_silu", st, stream)) != MOE_OK) return rc;
     if (flags & MOE_FLAG_ATOMIC_COMBINE) {
       st = moe::launch_zero(out, T * H, stream);
       if ((rc = stage_check(flags, "zero_out", st, stream)) != MOE_OK) return rc;
       st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
-                                            tile_expert, num_tiles, topk_weights, H, I, K,
-                                            L.max_tiles, nullptr, out, ep.b2, stream)
+                                            tile_expert, num_tiles, topk_weights, H, I, E,
+                                            K, L.max_tiles, nullptr, out, ep.b2, stream)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
-                                        topk_weights, H, I, K, L.max_tiles, nullptr, out, ep.b2,
-                                        stream);
+                                        topk_weights, H, I, E, K, L.max_tiles, nullptr, out,
+                                        ep.b2, stream);
       if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
     } else {
       float* y = at<float>(ws, L.y);
       st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
-                                            tile_expert, num_tiles, topk_weights, H, I, K,
-                                            L.max_tiles, y, nullptr, nullptr, stream, L.ks2,
+                                            tile_expert, num_tiles, topk_weights, H, I, E,
+                                            K, L.max_tiles, y, nullptr, nullptr, stream, L.ks2,
                                             T * K)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
-                                        topk_weights, H, I, K, L.max_tiles, y, nullptr, nullptr,
-                                        stream, L.ks2, T * K);
+                                        topk_weights, H, I, E, K, L.max_tiles, y, nullptr,
+                                        nullptr, stream, L.ks2, T * K);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
       st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2, out,
                                stream, L.ks2);
@@ -556,8 +575,8 @@ int moe_gemm1_silu(const void* hidden, const void* w1, const int32_t* sorted,
   if (!hidden || !w1 || !sorted || !tile_expert || !num_tiles || !act)
     return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
   hipError_t st = moe::launch_gemm1_silu(
-      moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256}, static_cast<const uint16_t*>(hidden),
-      static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
+      gemm1_entry_cfg(T, H, I, E, K, m_tile), static_cast<const uint16_t*>(hidden),
+      static_cast<const uint16_t*>(w1), sorted, tile_expert, num_tiles, T, H, I, E, K, max_tiles,
       static_cast<uint16_t*>(act), moe::Epilogue{}, static_cast<hipStream_t>(stream));
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu", st);
 }
@@ -582,8 +601,8 @@ int moe_gemm1_silu_fp8(const void* hidden, const uint8_t* w1q, const float* w1_s
   if (!hidden || !w1q || !w1_scale || !sorted || !tile_expert || !num_tiles || !act)
     return set_error(MOE_ERR_INVALID_ARG, "null device pointer");
   hipError_t st = moe::launch_gemm1_silu_fp8(
-      moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256}, static_cast<const uint16_t*>(hidden), w1q,
-      w1_scale, block, sorted, tile_expert, num_tiles, T, H, I, K, max_tiles,
+      gemm1_entry_cfg(T, H, I, E, K, m_tile), static_cast<const uint16_t*>(hidden), w1q,
+      w1_scale, block, sorted, tile_expert, num_tiles, T, H, I, E, K, max_tiles,
       static_cast<uint16_t*>(act), moe::Epilogue{}, static_cast<hipStream_t>(stream));
   return st == hipSuccess ? MOE_OK : hip_error("moe_gemm1_silu_fp8", st);
 }

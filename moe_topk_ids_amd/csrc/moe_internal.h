@@ -42,6 +42,8 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int
                         int32_t* tile_expert, int32_t* num_tiles, hipStream_t stream);
 
 // Tile configuration of the grouped GEMMs, chosen per problem on the host.
+// Every grouped GEMM skips a row tile whose tile_expert entry is outside
+// [0, E) rather than address weights past the end of w1/w2.
 struct GemmCfg {
   int bm;  // token rows per tile (the routing m_tile)
   int bn;  // weight rows per tile (GEMM1: half gate, half up)
@@ -58,20 +60,20 @@ bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block);
 hipError_t launch_gemm1_silu_fp8(GemmCfg cfg, const uint16_t* hidden, const uint8_t* w1q,
                                  const float* w1s, int64_t block, const int32_t* sorted,
                                  const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
-                                 int64_t H, int64_t I, int64_t K, int64_t max_tiles,
+                                 int64_t H, int64_t I, int64_t E, int64_t K, int64_t max_tiles,
                                  uint16_t* act, const Epilogue& ep, hipStream_t stream);
 hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q,
                             const float* w2s, int64_t block, const int32_t* sorted,
                             const int32_t* tile_expert, const int32_t* num_tiles,
-                            const float* topk_weights, int64_t H, int64_t I, int64_t K,
-                            int64_t max_tiles, float* y, float* out, const float* b2,
+                            const float* topk_weights, int64_t H, int64_t I, int64_t E,
+                            int64_t K, int64_t max_tiles, float* y, float* out, const float* b2,
                             hipStream_t stream, int ksplit = 1, int64_t n_slots = 0);
 
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
                              const int32_t* num_tiles, int64_t T, int64_t H, int64_t I,
-                             int64_t K, int64_t max_tiles, uint16_t* act, const Epilogue& ep,
-                             hipStream_t stream);
+                             int64_t E, int64_t K, int64_t max_tiles, uint16_t* act,
+                             const Epilogue& ep, hipStream_t stream);
 
 // Down projection. If `out` is non-null the tile results (plus b2[e], if
 // given) are scaled by the routing weight and atomically added to out[t, :];
@@ -79,8 +81,8 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
-                        int64_t I, int64_t K, int64_t max_tiles, float* y, float* out,
-                        const float* b2, hipStream_t stream, int ksplit = 1,
+                        int64_t I, int64_t E, int64_t K, int64_t max_tiles, float* y,
+                        float* out, const float* b2, hipStream_t stream, int ksplit = 1,
                         int64_t n_slots = 0);
 
 // Split of the down projection's contraction (1 or 2; see gemm.hip):

@@ -20,6 +20,7 @@
 // experts present and an LDS list of the expert's slots. Dot products use
 // the packed bf16 dot instruction (two products per lane per instruction,
 // fp32 accumulation), so weights and token rows stay packed in registers.
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,14 +30,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBitmapWords = kMaxExperts / 32;
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
-}
 // (the vector elements are copied to scalars first: a bit cast applied to a
 // vector element expression itself reads element 0 whatever the index)
 __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
@@ -46,29 +39,6 @@ __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
   acc = dot2(a1, b1, acc);
   acc = dot2(a2, b2, acc);
   return dot2(a3, b3, acc);
-}
-
-// v + the value DPP control `ctrl` moves into this lane (0 where row_mask
-// leaves a row out)
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
-                                            false);
-  return v + __builtin_bit_cast(float, m);
-}
-
-// Sum over aligned groups of G lanes with DPP moves (no LDS round trips).
-// The group's total ends up in its last lane (and, for G <= 16, in every
-// lane of the group).
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-  if (G >= 2) v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]: pairs
-  if (G >= 4) v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]: quads
-  if (G >= 8) v = dpp_add<0x141>(v);       // row_half_mirror: 8 lanes
-  if (G >= 16) v = dpp_add<0x140>(v);      // row_mirror: 16 lanes
-  if (G >= 32) v = dpp_add<0x142, 0xA>(v); // row_bcast:15 into rows 1, 3: 32 lanes
-  if (G >= 64) v = dpp_add<0x143, 0xC>(v); // row_bcast:31 into rows 2, 3: 64 lanes
-  return v;
 }
 
 // Shared prologue: find the expert this workgroup serves (the r-th expert
