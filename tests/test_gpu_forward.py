@@ -7,7 +7,7 @@ import moe_topk_ids_amd as moe
 import oracle
 from gpu_helpers import (REL_L2_BF16_INTER, assert_close, cpu_inputs, oracle_rows, rel_l2,
                          require_gpu, sample_rows, say, shape_inputs, to_device)
-from moe_topk_ids_amd.inputs import SHAPES, bf16_bits
+from moe_topk_ids_amd.inputs import SHAPES, Shape, bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +26,18 @@ def _run(dd, flags):
     return out.cpu().numpy()
 
 
-# Sampled token rows per workload for the oracle (full output for tiny).
-SAMPLES = {"tiny": 64, "prefill": 160, "decode": 1, "wide": 96, "large": 48}
+# Token rows per workload checked against the oracle: every row of tiny,
+# prefill and decode; 1024 seeded rows (first and last included) of wide and
+# large, which reach every row tile and every tile window of the persistent
+# schedule (wide: ~1090 row tiles of 64 rows, each holding slots of ~64
+# different tokens; large: ~124 tiles of 256 rows, 2048 slots sampled).
+SAMPLES = {"tiny": 64, "prefill": 4195, "decode": 1, "wide": 1024, "large": 1024}
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_forward_matches_oracle(name):
-    """Every combine path at the workload's full size; the oracle on sampled
-    token rows (all rows for tiny)."""
+    """Every combine path at the workload's full size against the oracle on
+    all token rows (tiny, prefill, decode) or 1024 seeded rows (wide, large)."""
     require_gpu()
     s = SHAPES[name]
     d = shape_inputs(name)
@@ -111,13 +115,24 @@ def test_small_batch_repeated_and_shared_experts():
                  "small-batch/shared")
 
 
-@pytest.mark.parametrize("name", ["tiny", "prefill", "wide"])
+# (workload, token rows checked): the forward's gate/up tiles 128x128
+# (tiny), 192x256 (prefill), 64x256 (wide) and 64x128 (the shapes-table row
+# T=135, H=I=2048, E=8, top-2)
+INTER_CASES = {"tiny": 64, "prefill": 1024, "wide": 512, "t135": 135}
+
+
+@pytest.mark.parametrize("name", list(INTER_CASES))
 def test_intermediate_matches_oracle(name):
-    """GEMM1 + SiLU intermediate vs the oracle's per-slot bf16 activation:
-    at most one bf16 ulp apart, nearly all identical."""
+    """GEMM1 + SiLU intermediate (the forward's own gate/up tile) vs the
+    oracle's per-slot bf16 activation: at most one bf16 ulp apart, nearly all
+    identical."""
     require_gpu()
-    s = SHAPES[name]
-    d = shape_inputs(name)
+    if name == "t135":
+        s = Shape("t135", 135, 2048, 2048, 8, 2)
+        d = cpu_inputs(s.T, s.H, s.I, s.E, s.K, seed=135)
+    else:
+        s = SHAPES[name]
+        d = shape_inputs(name)
     dd = to_device(d)
     M = moe.moe_m_tile(s.T, s.H, s.I, s.E, s.K)
     say(f"intermediate {name} M={M}")
@@ -125,7 +140,7 @@ def test_intermediate_matches_oracle(name):
     act = moe.moe_gemm1_silu(dd["hidden_states"], dd["w1"], r, s.K, M)
     torch.cuda.synchronize()
     slot_of = r["slot_of"].cpu().numpy()
-    rows = sample_rows(s.T, 48, seed=3)
+    rows = sample_rows(s.T, INTER_CASES[name], seed=3)
     slots = (rows[:, None] * s.K + np.arange(s.K)[None, :]).ravel()
     got = act.cpu().view(torch.int16).numpy().view(np.uint16)[slot_of[slots]]
     sub = {k: d[k] for k in d}
@@ -312,9 +327,9 @@ def test_caller_workspace_and_side_stream():
 
 
 def test_decode_path_with_caller_workspace_of_garbage():
-    """The decode path with a caller workspace full of arbitrary bytes (its
-    readiness counters included) gives the internal-workspace result, twice
-    in a row."""
+    """The decode path with a caller workspace full of arbitrary bytes gives
+    the internal-workspace result, twice in a row (the per-token kernels
+    write every activation value they read back)."""
     require_gpu()
     s = SHAPES["decode"]
     dd = to_device(shape_inputs("decode"))
@@ -331,8 +346,8 @@ def test_decode_path_with_caller_workspace_of_garbage():
 
 def test_decode_after_grouped_calls_and_back_to_back():
     """Grouped calls between decode calls share the internal workspace; 40
-    decode calls queued without a host sync (each advancing the readiness
-    counters) all give the same bits; so does the debug-sync flag."""
+    decode calls queued without a host sync all give the same bits; so does
+    the debug-sync flag."""
     require_gpu()
     dd = to_device(shape_inputs("decode"))
     tiny = to_device(shape_inputs("tiny"))
@@ -376,14 +391,15 @@ def test_debug_sync_flag():
 
 def test_largest_shapes_row():
     """The largest row of the shapes table (T=45936, H=2048, I=768, E=128,
-    top-8): full-size run, sampled rows against the oracle."""
+    top-8): full-size run, 1024 seeded rows (first and last included)
+    against the oracle."""
     require_gpu()
     T, H, I, E, K = 45936, 2048, 768, 128, 8
     d = cpu_inputs(T, H, I, E, K, seed=0)
     dd = to_device(d)
     say("forward largest shapes-table row")
     got = _run(dd, None)
-    rows = sample_rows(T, 32, seed=5)
+    rows = sample_rows(T, 1024, seed=5)
     assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
                  "shapes-row-14")
 

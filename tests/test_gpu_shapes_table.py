@@ -1,5 +1,6 @@
 """Every row of the atrex-bench #009 shapes table at full size through the
-default entry point; the oracle on sampled token rows."""
+default entry point; the oracle on min(T, 256) token rows of each (all rows
+of T=135, seeded samples with the first and last row otherwise)."""
 import functools
 
 import numpy as np
@@ -32,7 +33,7 @@ def test_shapes_table_row(row):
     out = moe.moe_forward(dd["hidden_states"].contiguous(), dd["w1"], dd["w2"],
                           dd["topk_weights"].contiguous(), dd["topk_ids"].contiguous())
     torch.cuda.synchronize()
-    rows = sample_rows(T, 12, seed=T)
+    rows = sample_rows(T, 256, seed=T)
     got = out.cpu().numpy()[rows]
     assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, True), f"T={T},H={H},I={I},E={E}")
     del dd, out

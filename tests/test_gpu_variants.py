@@ -76,7 +76,7 @@ def test_variant_on_every_path(path, act, kw, bias):
 ])
 def test_variant_at_workload_size(name, act, kw):
     """Full-size workloads on the default path, with biases; the oracle on
-    sampled token rows."""
+    256 seeded token rows (every row of decode)."""
     require_gpu()
     s = SHAPES[name]
     d = shape_inputs(name)
@@ -84,7 +84,7 @@ def test_variant_at_workload_size(name, act, kw):
     dd, bd = to_device(d), to_device(b)
     say(f"variant {act} at {name}")
     got = _run(dd, None, act, kw, bd)
-    rows = sample_rows(s.T, 32, seed=4)
+    rows = sample_rows(s.T, 256, seed=4)
     _check(got[rows], _oracle(d, rows, act, kw, b), _oracle(d, rows, act, kw, b, True),
            f"{name}/{act}")
 
