@@ -250,3 +250,18 @@ def bf16_to_f32(a: np.ndarray) -> np.ndarray:
     out = np.zeros(a.shape, np.float32)
     lib.oracle_bf16_to_f32(_ptr(a), _ptr(out), a.size)
     return out
+
+
+def omp_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS, else the
+    runtime's default)."""
+    lib = _load()
+    lib.omp_get_max_threads.restype = ctypes.c_int
+    return int(lib.omp_get_max_threads())
+
+
+def set_omp_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops started from this thread."""
+    lib = _load()
+    lib.omp_set_num_threads.argtypes = [ctypes.c_int]
+    lib.omp_set_num_threads(int(n))
