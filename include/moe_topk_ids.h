@@ -119,6 +119,29 @@ int moe_forward_ex(const void* hidden, const void* w1, const void* w2,
                    float* out, uint32_t flags, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * forward as moe_forward_ex (same kernels, same bits) with no allocation and
+ * no caller workspace: its workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES, which every GPU the library runs on holds from
+ * the first call on that device until the process ends. Sizes whose
+ * workspace (moe_workspace_bytes(T, H, I, E, K, flags)) exceeds it return
+ * MOE_ERR_WORKSPACE with a message naming both sizes; 128 MiB holds every
+ * per-token and small-batch call and grouped calls up to T=4195, H=I=2048,
+ * E=8, top-2. Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race;
+ * order them on one stream. The array keeps the last call's contents; no
+ * kernel relies on it starting at zero. Flags as moe_forward_ex (bf16
+ * weights; MOE_FLAG_VALIDATE_IDS and MOE_FLAG_DEBUG_SYNC synchronise the
+ * stream and so do not belong in a captured graph).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int moe_forward_noalloc(const void* hidden, const void* w1, const void* w2,
+                        const float* topk_weights, const int32_t* topk_ids,
+                        int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
+                        float* out, uint32_t flags, void* stream);
+
 /* Gated activations (the later tpu-inference fused_moe kernel.py,
  * activation_fn and swigluoai): */
 #define MOE_ACT_SILU 0      /* silu(g) * u                                    */

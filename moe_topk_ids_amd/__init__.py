@@ -34,6 +34,8 @@ ACT_GELU_ERF = 3
 ACTIVATIONS = {"silu": ACT_SILU, "gelu_tanh": ACT_GELU_TANH, "swigluoai": ACT_SWIGLUOAI,
                "gelu_erf": ACT_GELU_ERF}
 
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
 PATH_GROUPED = 0
 PATH_DECODE = 1
 PATH_SMALL_BATCH = 2
@@ -73,6 +75,8 @@ def load_library():
     lib.moe_forward_fp8.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, i64, i32, f32,
                                     f32, p, p, p, u32, p, sz, p]
     lib.moe_forward_fp8.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, u32, p]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, u32]
     lib.moe_workspace_bytes.restype = sz
     lib.moe_m_tile.argtypes = [i64, i64, i64, i64, i64, u32]

@@ -300,6 +300,10 @@ T* at(void* base, size_t off) {
 
 }  // namespace
 
+namespace moe {
+int set_last_error(int code, const char* msg) { return set_error(code, "%s", msg); }
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -9,6 +9,9 @@
 
 namespace moe {
 
+// Records the message moe_last_error() returns on this thread; returns code.
+int set_last_error(int code, const char* msg);
+
 // Slots handled by one routing workgroup (grows with T*K so that the number
 // of routing workgroups stays at most kRouteMaxBlocks).
 constexpr int kRouteThreads = 256;

@@ -31,7 +31,7 @@ def test_header_declares_the_api():
     for n in ("moe_forward", "moe_forward_ex", "moe_workspace_bytes", "moe_m_tile", "moe_route",
               "moe_route_scratch_bytes", "moe_gemm1_silu", "moe_last_error", "moe_release",
               "moe_uses_decode_path", "moe_topk_softmax", "moe_path", "moe_forward_act", "moe_forward_fp8",
-              "moe_gemm1_silu_fp8", "moe_fp8_widens_in_gemm"):
+              "moe_gemm1_silu_fp8", "moe_fp8_widens_in_gemm", "moe_forward_noalloc"):
         assert n in names
 
 
@@ -181,3 +181,19 @@ def test_path_choice(lib):
     # the small-batch workspace holds the bf16 activations and fp32 slot rows
     ws = moe.moe_workspace_bytes(100, 2048, 2048, 8, 2, fl)
     assert ws >= 200 * 2048 * 2 + 200 * 2048 * 4
+
+
+def test_noalloc_rejects_sizes_beyond_its_array_on_the_host(lib):
+    """moe_forward_noalloc checks its workspace need against the static
+    array before any device call: the large workload is refused with a
+    message naming both sizes; invalid sizes still get the size errors."""
+    p = ctypes.c_void_p(0)
+    rc = lib.moe_forward_noalloc(p, p, p, p, p, 15381, 4096, 4096, 8, 2, p, 0, p)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    msg = lib.moe_last_error().decode()
+    assert "static scratch" in msg and str(moe.NOALLOC_SCRATCH_BYTES) in msg
+    assert str(lib.moe_workspace_bytes(15381, 4096, 4096, 8, 2, 0)) in msg
+    assert lib.moe_forward_noalloc(p, p, p, p, p, 4, 128, 128, 2, 3, p, 0, p) == \
+        moe.MOE_ERR_INVALID_ARG
+    # prefill's workspace fits the array
+    assert 0 < lib.moe_workspace_bytes(4195, 2048, 2048, 8, 2, 0) <= moe.NOALLOC_SCRATCH_BYTES
