@@ -100,7 +100,15 @@ def route(ids: np.ndarray, E: int, M: int):
                 num_tiles=int(num_tiles[0]))
 
 
-def moe_forward(x, w1, w2, topk_weights, topk_ids, bf16_inter: bool = False) -> np.ndarray:
+def _mode(bf16_inter: bool, bf16_y: bool) -> int:
+    """The C oracle's mode bits: 1 rounds the activation to bf16, 2 rounds
+    each expert's down-projection result y_{t,k} to bf16 (before b2 and the
+    routing weight)."""
+    return (1 if bf16_inter else 0) | (2 if bf16_y else 0)
+
+
+def moe_forward(x, w1, w2, topk_weights, topk_ids, bf16_inter: bool = False,
+                bf16_y: bool = False) -> np.ndarray:
     """fp32 oracle forward. x uint16 [T,H]; w1 uint16 [E,2I,H]; w2 uint16 [E,H,I]."""
     lib = _load()
     x, w1, w2 = _c(x, np.uint16), _c(w1, np.uint16), _c(w2, np.uint16)
@@ -112,7 +120,7 @@ def moe_forward(x, w1, w2, topk_weights, topk_ids, bf16_inter: bool = False) -> 
     assert H2 == H and w2.shape == (E, H, I) and tw.shape == ids.shape == (T, K)
     out = np.zeros((T, H), np.float32)
     lib.oracle_moe_forward(_ptr(x), _ptr(w1), _ptr(w2), _ptr(tw), _ptr(ids), T, H, I, E, K,
-                           1 if bf16_inter else 0, _ptr(out))
+                           _mode(bf16_inter, bf16_y), _ptr(out))
     return out
 
 
@@ -143,7 +151,8 @@ def _optptr(a):
 
 
 def moe_forward_act(x, w1, w2, topk_weights, topk_ids, act: str = "silu", alpha: float = 1.702,
-                    limit: float = 7.0, b1=None, b2=None, bf16_inter: bool = False) -> np.ndarray:
+                    limit: float = 7.0, b1=None, b2=None, bf16_inter: bool = False,
+                    bf16_y: bool = False) -> np.ndarray:
     """fp32 oracle forward with an activation variant and optional fp32
     biases b1 [E, 2I] (gate, then up) and b2 [E, H]."""
     lib = _load()
@@ -159,7 +168,7 @@ def moe_forward_act(x, w1, w2, topk_weights, topk_ids, act: str = "silu", alpha:
     out = np.zeros((T, H), np.float32)
     lib.oracle_moe_forward_act(_ptr(x), _ptr(w1), _ptr(w2), _ptr(tw), _ptr(ids), T, H, I, E, K,
                                ACTIVATIONS[act], alpha, limit, _optptr(b1), _optptr(b2),
-                               1 if bf16_inter else 0, _ptr(out))
+                               _mode(bf16_inter, bf16_y), _ptr(out))
     return out
 
 
@@ -183,7 +192,7 @@ def moe_forward_act_f64(x, w1, w2, topk_weights, topk_ids, act: str = "silu",
 
 def moe_forward_q(x, w1q, w1s, w2q, w2s, block: int, topk_weights, topk_ids, act: str = "silu",
                   alpha: float = 1.702, limit: float = 7.0, b1=None, b2=None,
-                  bf16_inter: bool = False) -> np.ndarray:
+                  bf16_inter: bool = False, bf16_y: bool = False) -> np.ndarray:
     """fp32 oracle forward with FP8 E4M3 weights (uint8 codes) and fp32
     per-block scales: w1q [E,2I,H], w1s [E,2I,H/block], w2q [E,H,I],
     w2s [E,H,I/block]."""
@@ -202,7 +211,7 @@ def moe_forward_q(x, w1q, w1s, w2q, w2s, block: int, topk_weights, topk_ids, act
     out = np.zeros((T, H), np.float32)
     lib.oracle_moe_forward_q(_ptr(x), _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s), block,
                              _ptr(tw), _ptr(ids), T, H, I, E, K, ACTIVATIONS[act], alpha, limit,
-                             _optptr(b1), _optptr(b2), 1 if bf16_inter else 0, _ptr(out))
+                             _optptr(b1), _optptr(b2), _mode(bf16_inter, bf16_y), _ptr(out))
     return out
 
 

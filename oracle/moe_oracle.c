@@ -46,6 +46,19 @@
  * rounded to bf16 (round to nearest, ties to even) before the down
  * projection, mirroring the GPU's declared storage precision.
  *
+ * Modes (the `mode` argument of the fp32 forwards, a bit mask):
+ *   ORA_MODE_BF16_INTER (1)  the activation rounded to bf16, as above;
+ *   ORA_MODE_BF16_Y     (2)  each expert's down-projection result y_{t,k}
+ *                            rounded to bf16 (round to nearest, ties to even)
+ *                            before its bias b2 and its routing weight are
+ *                            applied, then accumulated in fp32 as before.
+ *                            [tpu-ffn2] tpu-inference fused_moe v1 kernel.py,
+ *                            dynamic_ffn2, brings the down projection's fp32
+ *                            results to bf16 before accumulating them (by bit
+ *                            truncation, with bf16 additions); the reading
+ *                            here keeps one round-to-nearest-even per y_{t,k}
+ *                            and fp32 accumulation.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math), so
  * every fp32 operation is a separately rounded IEEE operation.
  */
@@ -235,12 +248,18 @@ static void ora_expert_down_f32(const float* act, const uint16_t* w2e, int64_t H
  * (erf form); b1 fp32 [E, 2I] (gate biases, then up biases) or NULL; b2 fp32
  * [E, H] or NULL, added to y before the routing weight:
  *   out[t,h] = sum_k topk_weights[t,k] * (y_{t,k}[h] + b2[e,h]).
+ * mode: ORA_MODE_* bits (bf16 activation; bf16 y_{t,k} before b2 and w).
  */
+#define ORA_MODE_BF16_INTER 1
+#define ORA_MODE_BF16_Y 2
+
 void oracle_moe_forward_act(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
                             const float* topk_weights, const int32_t* topk_ids, int64_t T,
                             int64_t H, int64_t I, int64_t E, int64_t K, int act_kind,
                             float alpha, float limit, const float* b1, const float* b2,
-                            int bf16_inter, float* out) {
+                            int mode, float* out) {
+  const int bf16_inter = (mode & ORA_MODE_BF16_INTER) != 0;
+  const int bf16_y = (mode & ORA_MODE_BF16_Y) != 0;
 #pragma omp parallel
   {
     float* act = (float*)malloc((size_t)I * sizeof(float));
@@ -256,6 +275,8 @@ void oracle_moe_forward_act(const uint16_t* x, const uint16_t* w1, const uint16_
         ora_expert_act_f32(x + t * H, w1 + (int64_t)e * 2 * I * H, H, I, act_kind, alpha, limit,
                            b1 ? b1 + (int64_t)e * 2 * I : NULL, bf16_inter, act);
         ora_expert_down_f32(act, w2 + (int64_t)e * H * I, H, I, y);
+        if (bf16_y)
+          for (int64_t h = 0; h < H; ++h) y[h] = ora_bf16_to_f32(ora_f32_to_bf16_rne(y[h]));
         if (b2)
           for (int64_t h = 0; h < H; ++h) y[h] = y[h] + b2[(int64_t)e * H + h];
         for (int64_t h = 0; h < H; ++h) o[h] = o[h] + w * y[h];
@@ -268,10 +289,9 @@ void oracle_moe_forward_act(const uint16_t* x, const uint16_t* w1, const uint16_
 
 void oracle_moe_forward(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
                         const float* topk_weights, const int32_t* topk_ids, int64_t T,
-                        int64_t H, int64_t I, int64_t E, int64_t K, int bf16_inter,
-                        float* out) {
+                        int64_t H, int64_t I, int64_t E, int64_t K, int mode, float* out) {
   oracle_moe_forward_act(x, w1, w2, topk_weights, topk_ids, T, H, I, E, K, ORA_ACT_SILU, 0.0f,
-                         0.0f, NULL, NULL, bf16_inter, out);
+                         0.0f, NULL, NULL, mode, out);
 }
 
 /*
@@ -391,8 +411,10 @@ void oracle_moe_forward_q(const uint16_t* x, const uint8_t* w1q, const float* w1
                           const uint8_t* w2q, const float* w2s, int64_t block,
                           const float* topk_weights, const int32_t* topk_ids, int64_t T,
                           int64_t H, int64_t I, int64_t E, int64_t K, int act_kind, float alpha,
-                          float limit, const float* b1, const float* b2, int bf16_inter,
+                          float limit, const float* b1, const float* b2, int mode,
                           float* out) {
+  const int bf16_inter = (mode & ORA_MODE_BF16_INTER) != 0;
+  const int bf16_y = (mode & ORA_MODE_BF16_Y) != 0;
   float lut[256];
   for (int c = 0; c < 256; ++c) lut[c] = oracle_fp8_e4m3_to_f32((uint8_t)c);
   const int64_t nb1 = H / block, nb2 = I / block;
@@ -430,6 +452,7 @@ void oracle_moe_forward_q(const uint16_t* x, const uint8_t* w1q, const float* w1
           float acc = 0.0f;
           for (int64_t i = 0; i < I; ++i)
             acc = acc + act[i] * (lut[w2q[r * I + i]] * w2s[r * nb2 + i / block]);
+          if (bf16_y) acc = ora_bf16_to_f32(ora_f32_to_bf16_rne(acc));
           if (b2) acc = acc + b2[(int64_t)e * H + h];
           o[h] = o[h] + w * acc;
         }
