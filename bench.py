@@ -51,6 +51,9 @@ PATHS = {
     "atomic": moe.FLAG_FORCE_GROUPED | moe.FLAG_ATOMIC_COMBINE,
     "decode": moe.FLAG_FORCE_DECODE,
     "small_batch": moe.FLAG_FORCE_SMALL_BATCH,
+    # the default path with the expert outputs kept fp32 / rounded to bf16
+    "fp32_y": moe.FLAG_FP32_Y,
+    "bf16_y": moe.FLAG_BF16_Y,
 }
 PATH_NAMES = {moe.PATH_GROUPED: "grouped", moe.PATH_DECODE: "decode",
               moe.PATH_SMALL_BATCH: "small_batch"}
@@ -241,6 +244,7 @@ def bench_workload(name: str, args, flush: Flusher):
     rec = {
         "workload": f"{name}: T={s.T} H={s.H} I={s.I} E={s.E} top_k={s.K}",
         "path": path,
+        "y_bf16": moe.moe_y_bf16(s.T, s.H, s.I, s.E, s.K, flags),
         "us_per_call": st,
         "tflops": flop / st["mean"] / 1e6,
         "algorithmic_gbs": alg_bytes / st["mean"] / 1e3,
@@ -360,12 +364,15 @@ def bench_table(args):
     for (H, I, E, K), rows in groups.items():
         log(f"[table] H={H} I={I} E={E} K={K}")
         steps = lambda T: int(max(5, min(50, 3e5 / max(6.0 * T * K * H * I / 5e14 * 1e6, 20.0))))
-        us = _time_rows([r[0] for r in rows], H, I, E, K, {"default": 0}, steps, flush)
+        us = _time_rows([r[0] for r in rows], H, I, E, K, {"default": PATHS[args.path]}, steps,
+                        flush)
         for (T, _, _, _, _, t_sol, t_prod) in rows:
             u = us[(T, "default")]
             flop = 6.0 * T * K * H * I
+            fl = PATHS[args.path]
             rec = {"T": T, "H": H, "I": I, "E": E, "top_k": K, "us_per_call": u,
-                   "tflops": flop / u / 1e6, "path": PATH_NAMES[moe.moe_path(T, H, I, E, K)],
+                   "tflops": flop / u / 1e6, "path": PATH_NAMES[moe.moe_path(T, H, I, E, K, fl)],
+                   "y_bf16": moe.moe_y_bf16(T, H, I, E, K, fl),
                    "page_t_sol_us": t_sol, "page_t_prod_us": t_prod,
                    "speedup_vs_page_t_prod": t_prod / u}
             results.append(rec)

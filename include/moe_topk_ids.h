@@ -82,6 +82,15 @@ extern "C" {
  * moe_forward_fp8 (FP8 weights). moe_forward_fp8 sets it itself; the bf16
  * entry points ignore it. */
 #define MOE_FLAG_FP8_WEIGHTS 64u
+/* Expert outputs on the grouped path's default (slot) combine: with
+ * MOE_FLAG_BF16_Y each down-projection result y_{t,k} is stored rounded to
+ * bf16 (round to nearest even) and the weighted sum reads it back, half the
+ * bytes of fp32 rows; with MOE_FLAG_FP32_Y it stays fp32. Without either
+ * flag the library chooses (moe_y_bf16 says which). The bf16 rounding is
+ * the one tpu-inference's fused_moe kernel applies to its down projection's
+ * results: out[t] = sum_k w * (bf16(y_{t,k}) + b2[e_k]) in fp32, k order. */
+#define MOE_FLAG_BF16_Y 128u
+#define MOE_FLAG_FP32_Y 256u
 
 /* Paths, as returned by moe_path. A FORCE flag whose path does not support
  * the sizes falls back to the grouped path. */
@@ -211,6 +220,12 @@ int moe_uses_decode_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
 /* The MOE_PATH_* moe_forward_ex takes for these sizes and flags, or a
  * negative MOE_ERR_* code on invalid sizes. */
 int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
+
+/* 1 if moe_forward_ex (and moe_forward_act / moe_forward_fp8 with these
+ * flags) rounds each expert output y_{t,k} to bf16 before the weighted sum
+ * for these sizes and flags (grouped path, slot combine), 0 if it keeps
+ * them fp32, negative MOE_ERR_* on invalid sizes. */
+int moe_y_bf16(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
 
 /*
  * The routing step alone (the grouping that tpu-inference's start_a2a_scatter

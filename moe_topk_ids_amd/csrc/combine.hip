@@ -13,6 +13,7 @@
 // the same bits as the atomic path's 0 + a + b in either order (when the
 // down projection's contraction is not split: the atomic path never splits
 // it, and its partial rows would be summed before the weight here).
+#include "device_util.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -108,6 +109,89 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   }
 }
 
+// The same weighted sum over bf16 slot rows (each y_{t,k} rounded to bf16
+// once by the down projection): out[t, :] = sum over k, in order from zero,
+// of w[t,k] * (y16[t*K + k, :] + b2[e, :]). A lane covers NC groups of 8
+// columns of the row's blockIdx.y-th block of 2048 * NC columns: one
+// 16-byte load of 8 bf16 per slot row and group, widened exactly to fp32.
+template <int KP, int NC>
+__global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
+    const uint16_t* __restrict__ y16, const float* __restrict__ topk_weights,
+    const int32_t* __restrict__ slot_of, const int32_t* __restrict__ ids, int32_t E, int64_t T,
+    int64_t H, int32_t K, const float* __restrict__ b2, float* __restrict__ out) {
+#pragma clang fp contract(off)
+  const int64_t h8 = H / 8;
+  const uint4* y8 = reinterpret_cast<const uint4*>(y16);
+  const float4* b4 = reinterpret_cast<const float4*>(b2);
+  const int64_t c0 = (int64_t)blockIdx.y * kThreads * NC + threadIdx.x;
+  int64_t col[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = c0 + (int64_t)kThreads * i;
+    col[i] = c < h8 ? c : h8 - 1;  // lanes past the row end load a valid group
+  }
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    float o[NC][8];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[i][q] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KP) {
+      uint4 v[KP][NC];
+      float w[KP];
+      bool live[KP];
+      int32_t ev[KP];
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const int k = k0 + j < K ? k0 + j : K - 1;
+        const int64_t f = t * K + k;
+        const int32_t e = ids[f];
+        const bool in = (uint32_t)e < (uint32_t)E;
+        live[j] = k0 + j < K && (slot_of ? slot_of[f] >= 0 : in);
+        ev[j] = in ? e : 0;
+        w[j] = topk_weights[f];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) v[j][i] = y8[f * h8 + col[i]];
+      }
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          float yv[8] = {bf16lo(v[j][i].x), bf16hi(v[j][i].x), bf16lo(v[j][i].y),
+                         bf16hi(v[j][i].y), bf16lo(v[j][i].z), bf16hi(v[j][i].z),
+                         bf16lo(v[j][i].w), bf16hi(v[j][i].w)};
+          if (b2) {  // w * (y + b2[e]): the expert's bias before its routing weight
+            const float4 ba = b4[(int64_t)ev[j] * (H / 4) + 2 * col[i]];
+            const float4 bb = b4[(int64_t)ev[j] * (H / 4) + 2 * col[i] + 1];
+            yv[0] = yv[0] + ba.x;
+            yv[1] = yv[1] + ba.y;
+            yv[2] = yv[2] + ba.z;
+            yv[3] = yv[3] + ba.w;
+            yv[4] = yv[4] + bb.x;
+            yv[5] = yv[5] + bb.y;
+            yv[6] = yv[6] + bb.z;
+            yv[7] = yv[7] + bb.w;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float n = o[i][q] + w[j] * yv[q];
+            o[i][q] = live[j] ? n : o[i][q];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = c0 + (int64_t)kThreads * i;
+      if (c < h8) {
+        float4* dst = reinterpret_cast<float4*>(out + t * H) + 2 * c;
+        dst[0] = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+        dst[1] = make_float4(o[i][4], o[i][5], o[i][6], o[i][7]);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ out, int64_t n4) {
   for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < n4;
        q += (int64_t)gridDim.x * kThreads)
@@ -147,6 +231,34 @@ hipError_t launch_combine(const float* y, const float* topk_weights, const int32
   else MOE_COMBINE_NC(8);
 #undef MOE_COMBINE_NC
 #undef MOE_COMBINE
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const uint16_t* y16, const float* topk_weights,
+                               const int32_t* slot_of, const int32_t* topk_ids, int64_t E,
+                               int64_t T, int64_t H, int64_t K, const float* b2, float* out,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int64_t nc = (H / 8 + kThreads - 1) / kThreads;  // 8-column groups per lane
+  // rows wider than 16384 floats: column blocks along grid.y
+  const dim3 grid((unsigned)(T < 2048 ? T : 2048), (unsigned)((nc + 3) / 4));
+#define MOE_COMBINE16(KP, NC)                                                               \
+  combine_bf16_kernel<KP, NC><<<grid, kThreads, 0, stream>>>(y16, topk_weights, slot_of,     \
+                                                             topk_ids, (int32_t)E, T, H,     \
+                                                             (int32_t)K, b2, out)
+#define MOE_COMBINE16_NC(KP)               \
+  do {                                     \
+    if (nc <= 1) MOE_COMBINE16(KP, 1);     \
+    else if (nc <= 2) MOE_COMBINE16(KP, 2); \
+    else MOE_COMBINE16(KP, 4);             \
+  } while (0)
+  // at most 16 loads of 16 bytes in flight per lane
+  if (K <= 1) MOE_COMBINE16_NC(1);
+  else if (K <= 2) MOE_COMBINE16_NC(2);
+  else if (K <= 4 || nc > 2) MOE_COMBINE16_NC(4);
+  else MOE_COMBINE16_NC(8);
+#undef MOE_COMBINE16_NC
+#undef MOE_COMBINE16
   return hipGetLastError();
 }
 

@@ -50,7 +50,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 
-enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2 };
+// kDownSlot writes fp32 slot rows; kDownSlotBf16 writes them rounded to bf16
+// (round to nearest even), half the bytes for the combine to read back.
+enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2, kDownSlotBf16 = 3 };
 
 struct GemmArgs {
   const uint16_t* a;        // token operand: hidden [T,H] (gathered) or act [P,I]
@@ -59,7 +61,7 @@ struct GemmArgs {
   const int32_t* tile_expert;
   const int32_t* num_tiles;
   const float* topk_weights;
-  void* out;                // act bf16 [P,I] | y fp32 [T*K,H] | out fp32 [T,H]
+  void* out;                // act bf16 [P,I] | y fp32 or bf16 [T*K,H] | out fp32 [T,H]
   int64_t kdim;             // contraction length (H or I)
   int64_t n_out;            // output columns (I for GEMM1, H for GEMM2)
   int64_t w_expert_stride;  // elements per expert in w
@@ -212,6 +214,29 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
             v.y = pack_bf16x2(a[2], a[3]);
             *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
           }
+        }
+      }
+    }
+  } else if (MODE == kDownSlotBf16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(args.out);
+    int32_t fr[TM];  // slot of each row, all looked up before the stores
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) fr[tm] = args.sorted[m0 + wm * WTM + tm * 32 + (lane & 31)];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int32_t f = fr[tm];
+      if (f < 0) continue;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int64_t col = (int64_t)ntile * BN + wn * WTN + tn * 32 + csub;
+        if (col >= args.n_out) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16_t& a = acc[tn][tm];
+          uint2 v;
+          v.x = pack_bf16x2(a[4 * j], a[4 * j + 1]);
+          v.y = pack_bf16x2(a[4 * j + 2], a[4 * j + 3]);
+          *reinterpret_cast<uint2*>(dst + (int64_t)f * args.n_out + col + 8 * j) = v;
         }
       }
     }
@@ -759,8 +784,9 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t E, int64_t K, int64_t max_tiles, float* y,
                         float* out, const float* b2, hipStream_t stream, int ksplit,
-                        int64_t n_slots) {
+                        int64_t n_slots, uint16_t* y16) {
   if (out && ksplit > 1) return hipErrorInvalidValue;  // atomic adds of partial sums
+  if (y16 && (out || ksplit > 1)) return hipErrorInvalidValue;  // whole rows, rounded once
   GemmArgs a{};
   a.n_experts = (int32_t)E;
   a.ksplit = ksplit;
@@ -772,7 +798,7 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   a.tile_expert = tile_expert;
   a.num_tiles = num_tiles;
   a.topk_weights = topk_weights;
-  a.out = out ? (void*)out : (void*)y;
+  a.out = out ? (void*)out : y16 ? (void*)y16 : (void*)y;
   a.kdim = I;
   a.n_out = H;
   a.w_expert_stride = H * I;
@@ -781,6 +807,7 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   a.max_tiles = (int32_t)max_tiles;
   a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
   if (out) return dispatch<kDownAtomic, false>(cfg, a, stream);
+  if (y16) return dispatch<kDownSlotBf16, false>(cfg, a, stream);
   return dispatch<kDownSlot, false>(cfg, a, stream);
 }
 
@@ -826,9 +853,10 @@ hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q
                             const int32_t* tile_expert, const int32_t* num_tiles,
                             const float* topk_weights, int64_t H, int64_t I, int64_t E,
                             int64_t K, int64_t max_tiles, float* y, float* out, const float* b2,
-                            hipStream_t stream, int ksplit, int64_t n_slots) {
+                            hipStream_t stream, int ksplit, int64_t n_slots, uint16_t* y16) {
   if (!fp8_gemm_supported(H, I, block)) return hipErrorInvalidValue;
   if (out && ksplit > 1) return hipErrorInvalidValue;
+  if (y16 && (out || ksplit > 1)) return hipErrorInvalidValue;
   GemmArgs a{};
   a.n_experts = (int32_t)E;
   a.ksplit = ksplit;
@@ -843,7 +871,7 @@ hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q
   a.tile_expert = tile_expert;
   a.num_tiles = num_tiles;
   a.topk_weights = topk_weights;
-  a.out = out ? (void*)out : (void*)y;
+  a.out = out ? (void*)out : y16 ? (void*)y16 : (void*)y;
   a.kdim = I;
   a.n_out = H;
   a.w_expert_stride = H * I;
@@ -852,6 +880,7 @@ hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q
   a.max_tiles = (int32_t)max_tiles;
   a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
   if (out) return dispatch<kDownAtomic, true>(cfg, a, stream);
+  if (y16) return dispatch<kDownSlotBf16, true>(cfg, a, stream);
   return dispatch<kDownSlot, true>(cfg, a, stream);
 }
 

@@ -165,6 +165,19 @@ moe::GemmCfg gemm1_entry_cfg(int64_t T, int64_t H, int64_t I, int64_t E, int64_t
   return moe::GemmCfg{m_tile, m_tile == 128 ? 128 : 256};
 }
 
+// Whether the grouped path's slot rows are stored as bf16, given the
+// contraction split the down projection would take with fp32 rows. The
+// flags decide when set. Otherwise bf16 rows, half the bytes written by the
+// down projection and read by the combine, unless the contraction is split
+// (the few-token rows of the E=8 shapes, whose slot rows are small; a split
+// needs fp32 partial rows summed before any rounding).
+bool y_bf16_choice(int ks2, uint32_t flags) {
+  if (flags & MOE_FLAG_ATOMIC_COMBINE) return false;
+  if (flags & MOE_FLAG_BF16_Y) return true;
+  if (flags & MOE_FLAG_FP32_Y) return false;
+  return ks2 == 1;
+}
+
 bool use_decode(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   return pick_path(T, H, I, E, K, flags) == MOE_PATH_DECODE;
 }
@@ -175,6 +188,7 @@ struct Layout {
   bool decode = false;
   moe::GemmCfg g1{}, g2{};
   int ks2 = 1;  // contraction split of the down projection
+  bool y16 = false;  // slot rows stored as bf16
   int64_t cap = 0, max_tiles = 0, nblk = 0;
   bool widened = false;       // room for bf16 copies of FP8 weights (grouped path)
   size_t w1dq = 0, w2dq = 0;
@@ -211,6 +225,8 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.ks2 = (flags & MOE_FLAG_ATOMIC_COMBINE)
               ? 1
               : moe::pick_ksplit(L.g2, T, K, E, (H + L.g2.bn - 1) / L.g2.bn, I);
+  L.y16 = y_bf16_choice(L.ks2, flags);
+  if (L.y16) L.ks2 = 1;  // bf16 rows are whole sums, rounded once
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
   L.nblk = moe::route_blocks(n);
@@ -222,7 +238,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.slot_of = take((size_t)n * 4);
   L.block_hist = take((size_t)E * L.nblk * 4);
   L.act = take((size_t)L.cap * I * 2);
-  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)L.ks2 * n * H * 4);
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)L.ks2 * n * H * (L.y16 ? 2 : 4));
   if ((flags & MOE_FLAG_FP8_WEIGHTS) && fp8_may_widen(T, H, I, E, K)) {
     L.widened = true;
     L.w1dq = take((size_t)E * 2 * I * H * 2);
@@ -331,6 +347,13 @@ int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fla
   const int rc = check_sizes(T, H, I, E, K);
   if (rc != MOE_OK) return rc;
   return pick_path(T, H, I, E, K, flags);
+}
+
+int moe_y_bf16(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return 0;
+  return make_layout(T, H, I, E, K, flags).y16 ? 1 : 0;
 }
 
 }  // extern "C"
@@ -449,17 +472,20 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                         ep.b2, stream);
       if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
     } else {
-      float* y = at<float>(ws, L.y);
+      float* y = L.y16 ? nullptr : at<float>(ws, L.y);
+      uint16_t* y16 = L.y16 ? at<uint16_t>(ws, L.y) : nullptr;
       st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
                                             tile_expert, num_tiles, topk_weights, H, I, E,
                                             K, L.max_tiles, y, nullptr, nullptr, stream, L.ks2,
-                                            T * K)
+                                            T * K, y16)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, E, K, L.max_tiles, y, nullptr,
-                                        nullptr, stream, L.ks2, T * K);
+                                        nullptr, stream, L.ks2, T * K, y16);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
-      st = moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2, out,
-                               stream, L.ks2);
+      st = L.y16 ? moe::launch_combine_bf16(y16, topk_weights, slot_of, topk_ids, E, T, H, K,
+                                            ep.b2, out, stream)
+                 : moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2,
+                                       out, stream, L.ks2);
       if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
     }
   }

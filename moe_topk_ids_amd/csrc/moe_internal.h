@@ -70,7 +70,8 @@ hipError_t launch_gemm2_fp8(GemmCfg cfg, const uint16_t* act, const uint8_t* w2q
                             const int32_t* tile_expert, const int32_t* num_tiles,
                             const float* topk_weights, int64_t H, int64_t I, int64_t E,
                             int64_t K, int64_t max_tiles, float* y, float* out, const float* b2,
-                            hipStream_t stream, int ksplit = 1, int64_t n_slots = 0);
+                            hipStream_t stream, int ksplit = 1, int64_t n_slots = 0,
+                            uint16_t* y16 = nullptr);
 
 hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t* w1,
                              const int32_t* sorted, const int32_t* tile_expert,
@@ -80,13 +81,14 @@ hipError_t launch_gemm1_silu(GemmCfg cfg, const uint16_t* hidden, const uint16_t
 
 // Down projection. If `out` is non-null the tile results (plus b2[e], if
 // given) are scaled by the routing weight and atomically added to out[t, :];
-// otherwise they are written unscaled and unbiased to y[f, :] (f = t*K + k).
+// otherwise they are written unscaled and unbiased to y[f, :] (f = t*K + k),
+// or, if `y16` is non-null (no split), rounded to bf16 into y16[f, :].
 hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* sorted, const int32_t* tile_expert,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t E, int64_t K, int64_t max_tiles, float* y,
                         float* out, const float* b2, hipStream_t stream, int ksplit = 1,
-                        int64_t n_slots = 0);
+                        int64_t n_slots = 0, uint16_t* y16 = nullptr);
 
 // Split of the down projection's contraction (1 or 2; see gemm.hip):
 // with ksplit > 1, launch_gemm2 writes ksplit partial slot buffers y + s*n_slots*H.
@@ -100,6 +102,11 @@ int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, i
 hipError_t launch_combine(const float* y, const float* topk_weights, const int32_t* slot_of,
                           const int32_t* topk_ids, int64_t E, int64_t T, int64_t H, int64_t K,
                           const float* b2, float* out, hipStream_t stream, int ksplit = 1);
+// The same weighted sum over bf16 slot rows y16 [T*K, H] (no split).
+hipError_t launch_combine_bf16(const uint16_t* y16, const float* topk_weights,
+                               const int32_t* slot_of, const int32_t* topk_ids, int64_t E,
+                               int64_t T, int64_t H, int64_t K, const float* b2, float* out,
+                               hipStream_t stream);
 hipError_t launch_zero(float* out, int64_t n, hipStream_t stream);
 
 // Sets *err_flag to 1 if any id is outside [0, E) or repeats within a token.

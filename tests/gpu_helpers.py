@@ -16,7 +16,9 @@ from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_inputs
 # intermediate): max-abs 2e-2 and relative L2 1e-2. Against the oracle in
 # bf16-intermediate mode (the GPU's declared storage precision) the only
 # differences left are fp32 summation order and activations that round to
-# the neighbouring bf16 value, so a much tighter relative L2 holds.
+# the neighbouring bf16 value, so a much tighter relative L2 holds. Where
+# the forward also rounds each expert output y_{t,k} to bf16, that oracle
+# does the same (tight_rows).
 MAX_ABS = 2e-2
 REL_L2 = 1e-2
 REL_L2_BF16_INTER = 2e-3
@@ -55,13 +57,32 @@ def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:
     return np.sort(np.concatenate([[0, T - 1], mid]))
 
 
-def oracle_rows(d: dict, rows: np.ndarray, bf16_inter: bool = False) -> np.ndarray:
+def oracle_rows(d: dict, rows: np.ndarray, bf16_inter: bool = False,
+                bf16_y: bool = False) -> np.ndarray:
     """The oracle's output for a subset of token rows (each row of the
     output depends only on its own token)."""
     x = bf16_bits(d["hidden_states"])[rows]
     return oracle.moe_forward(x, bf16_bits(d["w1"]), bf16_bits(d["w2"]),
                               d["topk_weights"].numpy()[rows], d["topk_ids"].numpy()[rows],
-                              bf16_inter=bf16_inter)
+                              bf16_inter=bf16_inter, bf16_y=bf16_y)
+
+
+def y_bf16_for(d: dict, flags) -> bool:
+    """Whether the forward with these flags rounds each expert output to
+    bf16 for the sizes of input set d (the library's own answer)."""
+    import moe_topk_ids_amd as moe
+
+    T, H = d["hidden_states"].shape
+    w1 = d["w1"] if "w1" in d else d["w1q"]
+    E, I2, _ = w1.shape
+    K = d["topk_ids"].shape[1]
+    return moe.moe_y_bf16(T, H, I2 // 2, E, K, flags or 0)
+
+
+def tight_rows(d: dict, rows: np.ndarray, flags) -> np.ndarray:
+    """The oracle in the GPU's declared storage precisions for this call:
+    bf16 activation, and bf16 expert outputs where the forward rounds them."""
+    return oracle_rows(d, rows, bf16_inter=True, bf16_y=y_bf16_for(d, flags))
 
 
 def rel_l2(a, b) -> float:

@@ -133,9 +133,23 @@ def test_router_argument_validation(lib):
 def test_workspace_and_tile_queries(lib):
     assert moe.moe_workspace_bytes(0, 512, 256, 8, 2) == 0
     ws_slot = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2)
+    ws_fp32 = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, moe.FLAG_FP32_Y)
     ws_atomic = moe.moe_workspace_bytes(4195, 2048, 2048, 8, 2, moe.FLAG_ATOMIC_COMBINE)
-    # the slot path holds the fp32 per-slot outputs [T*K, H]
-    assert ws_slot - ws_atomic >= 4195 * 2 * 2048 * 4
+    # the slot path holds the per-slot outputs [T*K, H]: bf16 by default
+    # here, fp32 with the flag; the atomic path none
+    assert moe.moe_y_bf16(4195, 2048, 2048, 8, 2)
+    assert not moe.moe_y_bf16(4195, 2048, 2048, 8, 2, moe.FLAG_FP32_Y)
+    assert not moe.moe_y_bf16(4195, 2048, 2048, 8, 2, moe.FLAG_ATOMIC_COMBINE)
+    assert ws_slot - ws_atomic >= 4195 * 2 * 2048 * 2
+    assert ws_fp32 - ws_atomic >= 4195 * 2 * 2048 * 4
+    # the split down projection of few-token E=8 rows keeps fp32 partial rows,
+    # unless bf16 rows are asked for (then no split)
+    assert not moe.moe_y_bf16(135, 2048, 2048, 8, 2)
+    assert moe.moe_y_bf16(135, 2048, 2048, 8, 2, moe.FLAG_BF16_Y)
+    assert (moe.moe_workspace_bytes(135, 2048, 2048, 8, 2)
+            > moe.moe_workspace_bytes(135, 2048, 2048, 8, 2, moe.FLAG_BF16_Y))
+    # the streaming paths keep fp32
+    assert not moe.moe_y_bf16(1, 2048, 768, 128, 8)
     assert moe.moe_m_tile(4195, 2048, 2048, 8, 2) in (64, 128, 192, 256)
     assert moe.moe_uses_decode_path(1, 2048, 768, 128, 8)
     assert not moe.moe_uses_decode_path(4195, 2048, 2048, 8, 2)

@@ -6,7 +6,8 @@ import torch
 import moe_topk_ids_amd as moe
 import oracle
 from gpu_helpers import (REL_L2_BF16_INTER, assert_close, cpu_inputs, oracle_rows, rel_l2,
-                         require_gpu, sample_rows, say, shape_inputs, to_device)
+                         require_gpu, sample_rows, say, shape_inputs, tight_rows, to_device,
+                         y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, Shape, bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -44,11 +45,15 @@ def test_forward_matches_oracle(name):
     dd = to_device(d)
     rows = sample_rows(s.T, SAMPLES[name], seed=1)
     want = oracle_rows(d, rows)
-    want_b16 = oracle_rows(d, rows, bf16_inter=True)
-    for path in ("default", "slot", "atomic"):
-        say(f"forward {name} path={path}")
-        got = _run(dd, None if path == "default" else PATHS[path])
-        assert_close(got[rows], want, want_b16, f"{name}/{path}")
+    tight = {}  # bf16 activation, expert outputs bf16 or fp32 as the path stores them
+    for path in ("default", "slot", "fp32_y", "atomic"):
+        fl = {"default": None, "fp32_y": PATHS["slot"] | moe.FLAG_FP32_Y}.get(path, PATHS.get(path))
+        yb = y_bf16_for(d, fl)
+        if yb not in tight:
+            tight[yb] = oracle_rows(d, rows, bf16_inter=True, bf16_y=yb)
+        say(f"forward {name} path={path} bf16_y={yb}")
+        got = _run(dd, fl)
+        assert_close(got[rows], want, tight[yb], f"{name}/{path}")
     del dd
 
 
@@ -65,7 +70,7 @@ def test_decode_path_matches_oracle(name):
     say(f"decode path on {name}")
     got = _run(dd, moe.FLAG_FORCE_DECODE)
     rows = sample_rows(got.shape[0], 64, seed=2)
-    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got[rows], oracle_rows(d, rows), tight_rows(d, rows, moe.FLAG_FORCE_DECODE),
                  f"decode-path/{name}")
 
 
@@ -88,7 +93,7 @@ def test_small_batch_path_matches_oracle(name):
     say(f"small-batch path on {name} (T={n})")
     got = _run(dd, moe.FLAG_FORCE_SMALL_BATCH)
     rows = sample_rows(n, 64, seed=3)
-    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got[rows], oracle_rows(d, rows), tight_rows(d, rows, moe.FLAG_FORCE_SMALL_BATCH),
                  f"small-batch/{name}")
     # the same slots on the per-token path: equal up to the order of the
     # fp32 dot products inside each row
@@ -111,7 +116,7 @@ def test_small_batch_repeated_and_shared_experts():
     d["topk_ids"] = ids.contiguous()
     rows = np.arange(512)
     got = _run(to_device(d), moe.FLAG_FORCE_SMALL_BATCH)
-    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got, oracle_rows(d, rows), tight_rows(d, rows, moe.FLAG_FORCE_SMALL_BATCH),
                  "small-batch/shared")
 
 
@@ -198,8 +203,9 @@ def test_split_down_projection(T, H, I, E, K):
     d = cpu_inputs(T, H, I, E, K, seed=135)
     dd = to_device(d)
     rows = np.arange(T)
+    assert not y_bf16_for(d, PATHS["slot"])  # a split keeps fp32 partial rows
     a = _run(dd, PATHS["slot"])
-    assert_close(a, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(a, oracle_rows(d, rows), tight_rows(d, rows, PATHS["slot"]),
                  f"split T={T} I={I}")
     b = _run(dd, PATHS["slot"])
     assert np.array_equal(a, b)
@@ -219,13 +225,13 @@ def test_atomic_path_is_deterministic_for_top2(name):
     """With two routing terms per token the atomic combine is 0 + a + b in
     either order, two-term addition commutes and the hardware atomic add
     rounds to nearest even: run-to-run identical bits, and the same bits as
-    the slot path's (0 + a) + b."""
+    the slot path's (0 + a) + b with fp32 slot rows."""
     require_gpu()
     dd = to_device(shape_inputs(name))
     a = _run(dd, PATHS["atomic"])
     b = _run(dd, PATHS["atomic"])
     assert np.array_equal(a, b)
-    c = _run(dd, PATHS["slot"])
+    c = _run(dd, PATHS["slot"] | moe.FLAG_FP32_Y)
     assert np.array_equal(a, c)
 
 
@@ -241,7 +247,7 @@ def test_ragged_and_degenerate_shapes(T, H, I, E, K, path):
     say(f"shape T={T} H={H} I={I} E={E} K={K} path={path}")
     got = _run(dd, PATHS[path])
     rows = np.arange(T)
-    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got, oracle_rows(d, rows), tight_rows(d, rows, PATHS[path]),
                  f"{T},{H},{I},{E},{K}/{path}")
 
 
@@ -256,7 +262,7 @@ def test_all_tokens_one_expert_and_empty_experts():
     rows = np.arange(700)
     want = oracle_rows(d, rows)
     for path in ("slot", "atomic", "small_batch"):
-        assert_close(_run(dd, PATHS[path]), want, oracle_rows(d, rows, bf16_inter=True),
+        assert_close(_run(dd, PATHS[path]), want, tight_rows(d, rows, PATHS[path]),
                      f"one-expert/{path}")
 
 
@@ -377,7 +383,7 @@ def test_decode_tokens_are_independent(shape):
                 for k, v in dd.items()}, fl)
     assert np.array_equal(one[0], two[0])
     rows = np.arange(2)
-    assert_close(two, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(two, oracle_rows(d, rows), tight_rows(d, rows, fl),
                  f"decode-two-tokens/{shape}")
 
 
@@ -400,7 +406,7 @@ def test_largest_shapes_row():
     say("forward largest shapes-table row")
     got = _run(dd, None)
     rows = sample_rows(T, 1024, seed=5)
-    assert_close(got[rows], oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got[rows], oracle_rows(d, rows), tight_rows(d, rows, None),
                  "shapes-row-14")
 
 
@@ -426,9 +432,10 @@ def test_extreme_sizes(T, H, I, E, K, path):
     d = cpu_inputs(T, H, I, E, K, seed=T + H)
     dd = to_device(d)
     say(f"extreme T={T} H={H} I={I} E={E} K={K} path={path}")
-    got = _run(dd, None if path == "default" else PATHS[path])
+    fl = None if path == "default" else PATHS[path]
+    got = _run(dd, fl)
     rows = np.arange(T)
-    assert_close(got, oracle_rows(d, rows), oracle_rows(d, rows, bf16_inter=True),
+    assert_close(got, oracle_rows(d, rows), tight_rows(d, rows, fl),
                  f"extreme {T},{H},{I},{E},{K}/{path}")
 
 
@@ -450,3 +457,45 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):  # unknown activation
         moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
                         dd["topk_ids"], activation="relu")
+
+
+@pytest.mark.parametrize("name", ["prefill", "wide"])
+def test_bf16_expert_outputs_against_fp32_rows(name):
+    """The slot path with bf16 expert outputs against the same path with fp32
+    ones: every output within sum_k |w_k| * |y_k| * 2^-8 (half a bf16 ulp per
+    term) of the fp32 one, where y_k comes from the fp32-row run of a single
+    slot; both bitwise run-to-run stable."""
+    require_gpu()
+    s = SHAPES[name]
+    d = shape_inputs(name)
+    dd = to_device(d)
+    fl16 = PATHS["slot"] | moe.FLAG_BF16_Y
+    fl32 = PATHS["slot"] | moe.FLAG_FP32_Y
+    a16, a32 = _run(dd, fl16), _run(dd, fl32)
+    assert np.array_equal(a16, _run(dd, fl16))
+    bound = np.zeros((s.T, s.H))
+    for k in range(s.K):  # |y_k|: one slot per token, weight 1, fp32 rows
+        one = dict(dd, topk_ids=dd["topk_ids"][:, k:k + 1].contiguous(),
+                   topk_weights=torch.ones((s.T, 1), dtype=torch.float32, device="cuda"))
+        yk = _run(one, fl32)
+        bound += np.abs(d["topk_weights"].numpy()[:, k:k + 1]) * np.abs(yk) * 2.0 ** -8 * 1.001
+    diff = np.abs(a16.astype(np.float64) - a32)
+    slack = 1e-6 * np.max(np.abs(a32))
+    say(f"bf16 vs fp32 expert outputs {name}: max diff {diff.max():.3e}, "
+        f"max diff / bound {np.max(diff / (bound + slack)):.3f}, "
+        f"differing {np.mean(a16 != a32):.3f}")
+    assert np.all(diff <= bound + slack)
+
+
+def test_bf16_expert_outputs_forced_on_a_split_shape():
+    """T=135, H=I=2048, E=8, top-2 splits the down projection with fp32 rows;
+    asking for bf16 rows drops the split and matches the oracle's bf16-output
+    mode on every row."""
+    require_gpu()
+    T, H, I, E, K = 135, 2048, 2048, 8, 2
+    d = cpu_inputs(T, H, I, E, K, seed=135)
+    dd = to_device(d)
+    fl = PATHS["slot"] | moe.FLAG_BF16_Y
+    assert y_bf16_for(d, fl) and not y_bf16_for(d, PATHS["slot"])
+    rows = np.arange(T)
+    assert_close(_run(dd, fl), oracle_rows(d, rows), tight_rows(d, rows, fl), "split+bf16 rows")

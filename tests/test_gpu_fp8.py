@@ -8,7 +8,7 @@ import torch
 import moe_topk_ids_amd as moe
 import oracle
 from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, rel_l2, require_gpu,
-                         sample_rows, say, shape_inputs, to_device)
+                         sample_rows, say, shape_inputs, to_device, y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_biases, make_fp8_weights
 
 pytestmark = pytest.mark.gpu
@@ -38,13 +38,15 @@ def _oracle(d, q, rows, kw, b, bf16_inter=False):
         b2=None if b is None else b["b2"].numpy(), bf16_inter=bf16_inter, **kw)
 
 
-def _oracle_widened(d, q, rows, kw, b):
+def _oracle_widened(d, q, rows, kw, b, flags):
+    """The grouped path's tight oracle: bf16-widened weights, bf16 activation,
+    expert outputs rounded to bf16 where the forward does."""
     w1, w2 = _widened(q, q["block"])
     return oracle.moe_forward_act(
         bf16_bits(d["hidden_states"])[rows], bf16_bits(w1), bf16_bits(w2),
         d["topk_weights"].numpy()[rows], d["topk_ids"].numpy()[rows],
         b1=None if b is None else b["b1"].numpy(), b2=None if b is None else b["b2"].numpy(),
-        bf16_inter=True, **kw)
+        bf16_inter=True, bf16_y=y_bf16_for(d, (flags or 0) | moe.FLAG_FP8_WEIGHTS), **kw)
 
 
 def _run(dd, qd, flags, kw, bd):
@@ -90,7 +92,7 @@ def test_fp8_on_every_path(path, act, kw, bias, block):
     # the streaming paths read the codes themselves; the grouped path works
     # on the bf16-widened weights
     tight = (_oracle(d, q, rows, okw, b, True) if path in ("decode", "small_batch")
-             else _oracle_widened(d, q, rows, okw, b))
+             else _oracle_widened(d, q, rows, okw, b, PATHS[path]))
     _check(got, want, tight, f"fp8/{act}/bias={bias}/block={block}/{path}")
 
 
@@ -109,7 +111,7 @@ def test_fp8_at_workload_size(name):
     want = _oracle(d, q, rows, {"act": "silu"}, None)
     path = moe.moe_path(s.T, s.H, s.I, s.E, s.K, moe.FLAG_FP8_WEIGHTS)
     tight = (_oracle(d, q, rows, {"act": "silu"}, None, True) if path != moe.PATH_GROUPED
-             else _oracle_widened(d, q, rows, {"act": "silu"}, None))
+             else _oracle_widened(d, q, rows, {"act": "silu"}, None, 0))
     _check(got[rows], want, tight, f"fp8/{name}")
 
 
@@ -129,7 +131,7 @@ def test_fp8_grouped_at_the_scale_block_limit(H, I, block, native):
     got = _run(dd, qd, moe.FLAG_FORCE_GROUPED, {}, None)
     rows = np.arange(T)
     want = _oracle(d, q, rows, {"act": "silu"}, None)
-    tight = _oracle_widened(d, q, rows, {"act": "silu"}, None)
+    tight = _oracle_widened(d, q, rows, {"act": "silu"}, None, moe.FLAG_FORCE_GROUPED)
     _check(got, want, tight, f"fp8/grouped H={H} I={I}")
 
 

@@ -8,7 +8,7 @@ import torch
 import moe_topk_ids_amd as moe
 import oracle
 from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, rel_l2, require_gpu,
-                         sample_rows, say, shape_inputs, to_device)
+                         sample_rows, say, shape_inputs, to_device, y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_biases
 
 pytestmark = pytest.mark.gpu
@@ -25,12 +25,12 @@ ACTS = [("silu", {}), ("gelu_tanh", {}), ("gelu_erf", {}),
         ("swigluoai", {"alpha": 1.702, "limit": 0.1}), ("swigluoai", {"alpha": 1.702, "limit": 7.0})]
 
 
-def _oracle(d, rows, act, kw, b, bf16_inter=False):
+def _oracle(d, rows, act, kw, b, bf16_inter=False, bf16_y=False):
     return oracle.moe_forward_act(
         bf16_bits(d["hidden_states"])[rows], bf16_bits(d["w1"]), bf16_bits(d["w2"]),
         d["topk_weights"].numpy()[rows], d["topk_ids"].numpy()[rows], act=act,
         b1=None if b is None else b["b1"].numpy(), b2=None if b is None else b["b2"].numpy(),
-        bf16_inter=bf16_inter, **kw)
+        bf16_inter=bf16_inter, bf16_y=bf16_y, **kw)
 
 
 def _check(got, want, want_b16, label):
@@ -64,7 +64,8 @@ def test_variant_on_every_path(path, act, kw, bias):
     bd = None if b is None else to_device(b)
     rows = np.arange(T)
     got = _run(dd, PATHS[path], act, kw, bd)
-    _check(got, _oracle(d, rows, act, kw, b), _oracle(d, rows, act, kw, b, True),
+    _check(got, _oracle(d, rows, act, kw, b),
+           _oracle(d, rows, act, kw, b, True, y_bf16_for(d, PATHS[path])),
            f"{act}{kw}/bias={bias}/{path}")
 
 
@@ -85,8 +86,8 @@ def test_variant_at_workload_size(name, act, kw):
     say(f"variant {act} at {name}")
     got = _run(dd, None, act, kw, bd)
     rows = sample_rows(s.T, 256, seed=4)
-    _check(got[rows], _oracle(d, rows, act, kw, b), _oracle(d, rows, act, kw, b, True),
-           f"{name}/{act}")
+    _check(got[rows], _oracle(d, rows, act, kw, b),
+           _oracle(d, rows, act, kw, b, True, y_bf16_for(d, None)), f"{name}/{act}")
 
 
 def test_silu_variant_entry_equals_plain_entry():
