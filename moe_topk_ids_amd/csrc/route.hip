@@ -46,6 +46,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(
   for (int e = tid; e < E; e += kRouteThreads) block_hist[(int64_t)e * nblk + blockIdx.x] = hist[e];
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int32_t dpp_add_i32(int32_t v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Sum over the wave (DPP moves, as group_sum in device_util.h), returned in
+// every lane.
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+  v = dpp_add_i32<0xB1>(v);
+  v = dpp_add_i32<0x4E>(v);
+  v = dpp_add_i32<0x141>(v);
+  v = dpp_add_i32<0x140>(v);
+  v = dpp_add_i32<0x142, 0xA>(v);
+  v = dpp_add_i32<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ inline uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -104,17 +121,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   const int64_t nblk = gridDim.x;
   const int64_t b = blockIdx.x;
 
-  // 1. per expert: total count and the count in earlier workgroups
-  for (int e = tid; e < E; e += kRouteThreads) {
-    const int32_t* h = block_hist + (int64_t)e * nblk;
-    int32_t s = 0, p = 0;
-    for (int64_t j = 0; j < nblk; ++j) {
-      const int32_t v = h[j];
-      p += (j < b) ? v : 0;
-      s += v;
+  // 1. per expert: total count and the count in earlier workgroups. A wave
+  //    takes experts wave, wave + kWaves, ... in batches of kBatch; its lanes
+  //    hold the histograms of workgroups lane and lane + 64 (at most
+  //    kRouteMaxBlocks = 128 of them), all loaded before the first sum.
+  constexpr int kBatch = 16;
+  for (int eb = wave; eb < E; eb += kWaves * kBatch) {
+    int32_t h0[kBatch], h1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = eb + u * kWaves;
+      const int32_t* h = block_hist + (int64_t)(e < E ? e : 0) * nblk;
+      h0[u] = (e < E && lane < nblk) ? h[lane] : 0;
+      h1[u] = (e < E && lane + 64 < nblk) ? h[lane + 64] : 0;
     }
-    tot[e] = s;
-    pre[e] = p;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = eb + u * kWaves;
+      const int32_t s = wave_sum_i32(h0[u] + h1[u]);
+      const int32_t p = wave_sum_i32((lane < b ? h0[u] : 0) + (lane + 64 < b ? h1[u] : 0));
+      if (lane == 0 && e < E) {
+        tot[e] = s;
+        pre[e] = p;
+      }
+    }
   }
   for (int i = tid; i < kWaves * E; i += kRouteThreads) run[i] = 0;
   __syncthreads();

@@ -12,9 +12,17 @@ from moe_topk_ids_amd.inputs import SHAPES
 pytestmark = pytest.mark.gpu
 
 
-def _lane_terms(E: int) -> int:
-    """Logits per lane in the router kernel (one wave per token)."""
-    return 1 if E <= 64 else 2 if E <= 128 else 4 if E <= 256 else 8 if E <= 512 else 16
+def _gpu_sum_depth(E: int) -> int:
+    """Roundings on the longest path of the router kernel's exp sum: each
+    token's group of G lanes holds EPL logits per lane (4 up to 64 experts,
+    8 up to 128, else 16; G the smallest power of two with EPL*G >= E); a
+    lane adds its terms in order, then log2(G) levels of a tree over the
+    group."""
+    epl = 4 if E <= 64 else 8 if E <= 128 else 16
+    G = 1
+    while epl * G < E:
+        G *= 2
+    return min(epl, E) - 1 + G.bit_length() - 1
 
 
 def ulp_bound(E: int, K: int, renormalize: bool) -> int:
@@ -24,17 +32,17 @@ def ulp_bound(E: int, K: int, renormalize: bool) -> int:
     in the oracle (same argument l - max on both sides), and a relative
     difference r being under r/u ulps:
     - unnormalised p = exp / denominator: the denominator sums E terms, in
-      order in the oracle ((E-1)u) and per lane then over 6 butterfly levels
-      on the GPU ((lane terms + 5)u); one division each. Bound:
-      (4+4+lane terms+5+1)u + (2+2+E-1+1)u.
+      order in the oracle ((E-1)u) and along the GPU kernel's tree
+      (_gpu_sum_depth(E) u); one division each. Bound:
+      (4 + 4 + depth + 1)u + (2 + 2 + E - 1 + 1)u.
     - renormalised w = p_k / sum_j p_j: the denominator is a common factor
-      and cancels; left are the exps, two divisions and the K-term sum in k
-      order, (2 eps + (K+2)u) per side: (2K+16)u.
+      and cancels; left are the exps, two divisions and a K-term sum (any
+      order: at most K-1 roundings), (2 eps + (K+2)u) per side: (2K+16)u.
     Two more ulps cover the second-order terms.
     """
     if renormalize:
         return 2 * K + 16 + 2
-    return E + _lane_terms(E) + 18 + 2
+    return E + _gpu_sum_depth(E) + 13 + 2
 
 
 def _ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
