@@ -158,11 +158,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // tile): lane holds, for token row (lane & 31) of sub-tile tm, the weight
 // columns 8*j + 4*(lane >> 5) + {0,1,2,3} of sub-tile tn, in
 // acc[tn][tm][4j..4j+3].
-template <int BM, int BN, int WTM, int WTN, int MODE>
+// STAGED (bf16 slot rows only): the tile leaves through LDS, which must hold
+// BM x BN bf16.
+template <int BM, int BN, int WTM, int WTN, int MODE, bool STAGED>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
                                               f32x16_t (&acc)[WTN / 32][WTM / 32], int64_t m0,
                                               int ntile, int e, int wm, int wn, int lane,
-                                              int split) {
+                                              int split, char* lds) {
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
   const int csub = 4 * (lane >> 5);
@@ -217,7 +219,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
         }
       }
     }
-  } else if (MODE == kDownSlotBf16) {
+  } else if (MODE == kDownSlotBf16 && !STAGED) {
+    // bf16 slot rows stored straight from the accumulators, 8 bytes per lane
     uint16_t* dst = reinterpret_cast<uint16_t*>(args.out);
     int32_t fr[TM];  // slot of each row, all looked up before the stores
 #pragma unroll
@@ -239,6 +242,54 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
           *reinterpret_cast<uint2*>(dst + (int64_t)f * args.n_out + col + 8 * j) = v;
         }
       }
+    }
+  } else if (MODE == kDownSlotBf16) {
+    // bf16 slot rows through LDS (free once every wave has read the last
+    // stage): each lane writes its 4-column groups, then every staged row
+    // leaves in 16-byte stores by consecutive lanes, so each line of a slot
+    // row is written once and a tile takes half the store instructions of
+    // 8-byte stores straight from the accumulators. The 16-byte chunks of a
+    // staged row are XOR-permuted by the row, so the 32 rows one write
+    // instruction covers spread over the banks.
+    constexpr int CPRO = BN / 8;    // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPRO;  // staged rows per store instruction
+    constexpr int NWE = (BM / WTM) * (BN / WTN);
+    constexpr int ITERS = BM / RPI / NWE;
+    static_assert(64 % CPRO == 0 && (BM / RPI) % NWE == 0, "staged output rows");
+    const int wave = wn * (BM / WTM) + wm;
+    __syncthreads();
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int r = wm * WTM + tm * 32 + (lane & 31);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const f32x16_t& a = acc[tn][tm];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = (wn * WTN + tn * 32) / 8 + j;  // chunk of columns 8j .. 8j+7
+          uint2 v;
+          v.x = pack_bf16x2(a[4 * j], a[4 * j + 1]);
+          v.y = pack_bf16x2(a[4 * j + 2], a[4 * j + 3]);
+          *reinterpret_cast<uint2*>(lds + r * (BN * 2) + ((c ^ (r % CPRO)) << 4) + (lane >> 5) * 8) =
+              v;
+        }
+      }
+    }
+    __syncthreads();
+    uint16_t* dst = reinterpret_cast<uint16_t*>(args.out);
+    const int64_t n0 = (int64_t)ntile * BN;
+    const int cl = lane % CPRO;
+    const bool col_ok = n0 + cl * 8 < args.n_out;
+    int32_t fr[ITERS];  // every slot lookup before the first store
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+      fr[it] = args.sorted[m0 + (wave + it * NWE) * RPI + lane / CPRO];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = (wave + it * NWE) * RPI + lane / CPRO;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + ((cl ^ (r % CPRO)) << 4));
+      if (fr[it] >= 0 && col_ok)
+        *reinterpret_cast<uint4*>(dst + (int64_t)fr[it] * args.n_out + n0 + cl * 8) = v;
     }
   } else {
     float* dst = reinterpret_cast<float*>(args.out) + (int64_t)split * args.part_stride;
@@ -594,7 +645,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
-    tile_epilogue<BM, BN, WTM, WTN, MODE>(args, acc, m0, ntile, e, wm, wn, lane, split);
+    // bf16 slot rows leave through the ring's LDS where the tile fits it
+    constexpr bool kStaged = MODE == kDownSlotBf16 && BM * BN * 2 <= NS * STAGE;
+    tile_epilogue<BM, BN, WTM, WTN, MODE, kStaged>(args, acc, m0, ntile, e, wm, wn, lane, split,
+                                                   smem);
   }  // persistent tile loop
 }
 
