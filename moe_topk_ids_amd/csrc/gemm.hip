@@ -158,8 +158,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // tile): lane holds, for token row (lane & 31) of sub-tile tm, the weight
 // columns 8*j + 4*(lane >> 5) + {0,1,2,3} of sub-tile tn, in
 // acc[tn][tm][4j..4j+3].
-// STAGED (bf16 slot rows only): the tile leaves through LDS, which must hold
-// BM x BN bf16.
+// XOR key of the 16-byte chunks of a row staged for the epilogue's stores
+// (CPR chunks per row): the 32 rows one write instruction covers land on
+// distinct 16-byte bank groups of each 256-byte bank window, two rows per
+// group (rows of 128 bytes share a window in pairs, hence row / 2 there).
+template <int CPR>
+__device__ __forceinline__ int stage_swz(int r) {
+  return CPR >= 16 ? r % CPR : (r / (16 / CPR)) % CPR;
+}
+
+// STAGED: the tile (the gate/up product's bf16 intermediate, or bf16 slot
+// rows) leaves through LDS, which must hold it.
 template <int BM, int BN, int WTM, int WTN, int MODE, bool STAGED>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
                                               f32x16_t (&acc)[WTN / 32][WTM / 32], int64_t m0,
@@ -171,6 +180,22 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
   if (MODE == kGateUpSilu) {
     uint16_t* act = reinterpret_cast<uint16_t*>(args.out);
     const int64_t n0g = (int64_t)ntile * (BN / 2);
+    // the tile's intermediate: BM rows x BN/2 bf16 columns; with STAGED it
+    // leaves through LDS (see the bf16 slot rows below)
+    constexpr int CPRO = BN / 16;  // 16-byte chunks per staged row
+    if constexpr (STAGED) __syncthreads();  // every wave is done with the last stage
+    // v: columns col + 8j .. col + 8j + 3 of token row r (tile row tm*32 +
+    // (lane & 31) of the wave, sub-tile tn)
+    auto emit = [&](int64_t r, int64_t col, int tm, int tn, int j, uint2 v) {
+      if constexpr (STAGED) {
+        const int rl = wm * WTM + tm * 32 + (lane & 31);
+        const int c = (wn * (WTN / 2) + tn * 32) / 8 + j;
+        *reinterpret_cast<uint2*>(lds + rl * (BN / 2 * 2) + ((c ^ stage_swz<CPRO>(rl)) << 4) +
+                                  (lane >> 5) * 8) = v;
+      } else {
+        *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+      }
+    };
     if (args.act == kActSilu && args.bias == nullptr) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -185,7 +210,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
             uint2 v;
             v.x = pack_bf16x2(silu_mul(g[4 * j + 0], u[4 * j + 0]), silu_mul(g[4 * j + 1], u[4 * j + 1]));
             v.y = pack_bf16x2(silu_mul(g[4 * j + 2], u[4 * j + 2]), silu_mul(g[4 * j + 3], u[4 * j + 3]));
-            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+            emit(r, col, tm, tn, j, v);
           }
         }
       }
@@ -214,9 +239,27 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
             uint2 v;
             v.x = pack_bf16x2(a[0], a[1]);
             v.y = pack_bf16x2(a[2], a[3]);
-            *reinterpret_cast<uint2*>(act + r * args.n_out + col + 8 * j) = v;
+            emit(r, col, tm, tn, j, v);
           }
         }
+      }
+    }
+    if constexpr (STAGED) {
+      // every staged row leaves in 16-byte stores by consecutive lanes (pad
+      // rows included: their zeros are part of the intermediate)
+      constexpr int RPI = 64 / CPRO;
+      constexpr int NWE = (BM / WTM) * (BN / WTN);
+      constexpr int ITERS = BM / RPI / NWE;
+      static_assert(64 % CPRO == 0 && (BM / RPI) % NWE == 0, "staged rows");
+      const int wave = wn * (BM / WTM) + wm;
+      const int cl = lane % CPRO;
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int r = (wave + it * NWE) * RPI + lane / CPRO;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN / 2 * 2) +
+                                                        ((cl ^ stage_swz<CPRO>(r)) << 4));
+        *reinterpret_cast<uint4*>(act + (m0 + r) * args.n_out + n0g + cl * 8) = v;
       }
     }
   } else if (MODE == kDownSlotBf16 && !STAGED) {
@@ -270,8 +313,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
           uint2 v;
           v.x = pack_bf16x2(a[4 * j], a[4 * j + 1]);
           v.y = pack_bf16x2(a[4 * j + 2], a[4 * j + 3]);
-          *reinterpret_cast<uint2*>(lds + r * (BN * 2) + ((c ^ (r % CPRO)) << 4) + (lane >> 5) * 8) =
-              v;
+          *reinterpret_cast<uint2*>(lds + r * (BN * 2) + ((c ^ stage_swz<CPRO>(r)) << 4) +
+                                    (lane >> 5) * 8) = v;
         }
       }
     }
@@ -287,7 +330,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int r = (wave + it * NWE) * RPI + lane / CPRO;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + ((cl ^ (r % CPRO)) << 4));
+      const uint4 v =
+          *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + ((cl ^ stage_swz<CPRO>(r)) << 4));
       if (fr[it] >= 0 && col_ok)
         *reinterpret_cast<uint4*>(dst + (int64_t)fr[it] * args.n_out + n0 + cl * 8) = v;
     }
@@ -645,8 +689,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #undef MOE_LOAD_FRAGS
 #undef MOE_ISSUE_STAGE
 
-    // bf16 slot rows leave through the ring's LDS where the tile fits it
-    constexpr bool kStaged = MODE == kDownSlotBf16 && BM * BN * 2 <= NS * STAGE;
+    // bf16 intermediates and bf16 slot rows leave through the ring's LDS
+    // where the tile fits it (the intermediate always does; with FP8 weights
+    // the gate/up kernel keeps direct stores: staging there spills)
+    constexpr bool kStaged = (MODE == kGateUpSilu && !Q && BM * BN <= NS * STAGE) ||
+                             (MODE == kDownSlotBf16 && BM * BN * 2 <= NS * STAGE);
     tile_epilogue<BM, BN, WTM, WTN, MODE, kStaged>(args, acc, m0, ntile, e, wm, wn, lane, split,
                                                    smem);
   }  // persistent tile loop
