@@ -54,6 +54,8 @@ PATHS = {
     # the default path with the expert outputs kept fp32 / rounded to bf16
     "fp32_y": moe.FLAG_FP32_Y,
     "bf16_y": moe.FLAG_BF16_Y,
+    # the default path with the down projection in one launch (no column-half tail)
+    "no_tail": moe.FLAG_NO_TAIL_SPLIT,
 }
 PATH_NAMES = {moe.PATH_GROUPED: "grouped", moe.PATH_DECODE: "decode",
               moe.PATH_SMALL_BATCH: "small_batch"}

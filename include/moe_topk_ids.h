@@ -91,6 +91,11 @@ extern "C" {
  * results: out[t] = sum_k w * (bf16(y_{t,k}) + b2[e_k]) in fp32, k order. */
 #define MOE_FLAG_BF16_Y 128u
 #define MOE_FLAG_FP32_Y 256u
+/* Grouped path: run the down projection in one launch even where its last
+ * round of 192- or 256-row tiles would leave half the chip idle (by default
+ * those tiles then run as column halves in a second launch). The results
+ * are the same bits either way; for measurement. */
+#define MOE_FLAG_NO_TAIL_SPLIT 512u
 
 /* Paths, as returned by moe_path. A FORCE flag whose path does not support
  * the sizes falls back to the grouped path. */
@@ -226,6 +231,12 @@ int moe_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fla
  * for these sizes and flags (grouped path, slot combine), 0 if it keeps
  * them fp32, negative MOE_ERR_* on invalid sizes. */
 int moe_y_bf16(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
+
+/* 1 if moe_forward_ex, for these sizes and flags, plans the down
+ * projection's last partial round as column halves in a second launch (see
+ * MOE_FLAG_NO_TAIL_SPLIT; the kernels confirm it from the routing's tile
+ * count), 0 if not, negative MOE_ERR_* on invalid sizes. */
+int moe_down_tail_split(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags);
 
 /*
  * The routing step alone (the grouping that tpu-inference's start_a2a_scatter

@@ -28,6 +28,7 @@ FLAG_FORCE_SMALL_BATCH = 32
 FLAG_FP8_WEIGHTS = 64
 FLAG_BF16_Y = 128
 FLAG_FP32_Y = 256
+FLAG_NO_TAIL_SPLIT = 512
 
 ACT_SILU = 0
 ACT_GELU_TANH = 1
@@ -89,6 +90,8 @@ def load_library():
     lib.moe_path.restype = ctypes.c_int
     lib.moe_y_bf16.argtypes = [i64, i64, i64, i64, i64, u32]
     lib.moe_y_bf16.restype = ctypes.c_int
+    lib.moe_down_tail_split.argtypes = [i64, i64, i64, i64, i64, u32]
+    lib.moe_down_tail_split.restype = ctypes.c_int
     lib.moe_route.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, i64, p, p]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route_scratch_bytes.argtypes = [i64, i64, i64]
@@ -288,6 +291,15 @@ def moe_y_bf16(T, H, I, E, K, flags=0) -> bool:
     """Whether the forward rounds each expert output y_{t,k} to bf16 before
     the weighted sum for these sizes and flags."""
     v = int(load_library().moe_y_bf16(T, H, I, E, K, flags))
+    if v < 0:
+        _check(v)
+    return bool(v)
+
+
+def moe_down_tail_split(T, H, I, E, K, flags=0) -> bool:
+    """Whether the forward plans the down projection's last partial round
+    as column halves in a second launch for these sizes and flags."""
+    v = int(load_library().moe_down_tail_split(T, H, I, E, K, flags))
     if v < 0:
         _check(v)
     return bool(v)

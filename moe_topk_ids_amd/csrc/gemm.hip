@@ -50,6 +50,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 
+// Workgroups of one round of the chip at one per CU (8 XCDs x 32 CUs).
+constexpr int kRound = 256;
+
 // kDownSlot writes fp32 slot rows; kDownSlotBf16 writes them rounded to bf16
 // (round to nearest even), half the bytes for the combine to read back.
 enum Mode { kGateUpSilu = 0, kDownSlot = 1, kDownAtomic = 2, kDownSlotBf16 = 3 };
@@ -79,6 +82,13 @@ struct GemmArgs {
   // to out + s*part_stride
   int32_t ksplit;
   int64_t part_stride;
+  // Column-half tail of a tile order whose last round of the chip would be
+  // at most half full (tiles of one workgroup per CU): phase 1 runs the whole
+  // rounds of `rounds_of` workgroups, phase 2 (a second launch, BN half the
+  // first's) runs the remaining tiles as two column halves each, so their
+  // round takes about half a tile's time. 0: every tile in one launch.
+  int32_t phase;
+  int32_t rounds_of;
   // epilogue variants: activation kind and swigluoai parameters (GEMM1),
   // bias b1 [E, 2I] (GEMM1) or b2 [E, H] (GEMM2 with the atomic combine)
   int32_t act;
@@ -429,27 +439,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     // together (one expert's weights and token rows, which the last-level
     // cache then serves to all of them), each on a contiguous run of S tiles
     // that share rows in its own L2. The last, partial window is shared out
-    // evenly over the XCDs.
+    // evenly over the XCDs. Only the routing's live row tiles are numbered,
+    // so the rounds are the live tiles' rounds.
     const int n_tiles = args.n_tiles;
-    const int per_split = args.max_tiles * n_tiles;
+    const int live_m = min(args.num_tiles[0], args.max_tiles);
+    // the tile order: live_m row tiles x n_ord column tiles (in phase 2 the
+    // phase-1 launch's, twice this launch's width); phase 1 keeps its whole
+    // rounds when the rest fills at most half a round, phase 2 takes that rest
+    const int n_ord = args.phase == 2 ? n_tiles / 2 : n_tiles;
+    const int ord_tiles = live_m * n_ord;
+    int whole = ord_tiles;
+    if (args.phase != 0) {
+      const int w = (ord_tiles / args.rounds_of) * args.rounds_of;
+      if (2 * (ord_tiles - w) <= args.rounds_of) whole = w;
+    }
+    const int per_split = args.phase == 2 ? 2 * (ord_tiles - whole) : whole;
     const int total = per_split * args.ksplit;
     const int S = args.xcd_slots;
     const int slot = vb / 8;
     const int nfull = total / (8 * S);
+    const int chunk = (total - nfull * 8 * S + 7) / 8;  // per XCD in the partial window
     const int pid = slot < nfull * S
                         ? (slot / S) * 8 * S + (vb % 8) * S + slot % S
-                        : nfull * 8 * S + (vb % 8) * ((total - nfull * 8 * S + 7) / 8) +
-                              (slot - nfull * S);
-    if (pid >= total) continue;
+                        : nfull * 8 * S + (vb % 8) * chunk + (slot - nfull * S);
+    // the grid was sized for every row tile the routing could produce: slots
+    // past the live tiles' share (which would repeat another XCD's) do nothing
+    if (pid >= total || (slot >= nfull * S && slot - nfull * S >= chunk)) continue;
     const int split = pid / per_split;  // the contraction split is the slowest index
     const int tpid = pid - split * per_split;
-    const int group = tpid / (args.group_m * n_tiles);
+    const int opid = args.phase == 2 ? whole + tpid / 2 : tpid;  // position in the tile order
+    const int group = opid / (args.group_m * n_ord);
     const int first_m = group * args.group_m;
-    const int gsize = min(args.max_tiles - first_m, args.group_m);
-    const int within = tpid - group * args.group_m * n_tiles;
+    const int gsize = min(live_m - first_m, args.group_m);
+    const int within = opid - group * args.group_m * n_ord;
     const int mt = first_m + within % gsize;
-    const int ntile = within / gsize;
-    if (mt >= args.num_tiles[0]) continue;
+    const int ntile = args.phase == 2 ? 2 * (within / gsize) + (tpid & 1) : within / gsize;
     const int e = args.tile_expert[mt];
     if ((uint32_t)e >= (uint32_t)args.n_experts) continue;
     const int64_t m0 = (int64_t)mt * BM;
@@ -702,12 +726,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MODE, bool Q>
 hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   if (a.ksplit < 1) a.ksplit = 1;
-  const int64_t total = (int64_t)a.max_tiles * a.n_tiles * a.ksplit;
+  // phase 2: at most two halves of each tile short of a round
+  const int64_t total =
+      a.phase == 2 ? 2 * (int64_t)a.rounds_of : (int64_t)a.max_tiles * a.n_tiles * a.ksplit;
   if (total == 0) return hipSuccess;
   const size_t scl_bytes = Q ? ((size_t)BN * (a.nqb | 1) + 64) * sizeof(float) : 0;
-  // workgroups one CU holds at once (LDS-bound: 160 KB per CU), 32 CUs per XCD
+  // workgroups one CU holds at once (LDS-bound: 160 KB per CU), 32 CUs per XCD;
+  // the column halves of a tail go one to a CU
   constexpr size_t kStageBytes = (size_t)BM * BK * 2 + (size_t)BN * BK * (Q ? 1 : 2);
-  const int64_t per_cu = (int64_t)((160 * 1024) / (NS * kStageBytes + scl_bytes));
+  const int64_t per_cu =
+      a.phase == 2 ? 1 : (int64_t)((160 * 1024) / (NS * kStageBytes + scl_bytes));
   a.xcd_slots = (int32_t)(32 * (per_cu < 1 ? 1 : per_cu));
   const int64_t S = a.xcd_slots, nfull = total / (8 * S);
   const int64_t blocks = 8 * (nfull * S + (total - nfull * 8 * S + 7) / 8);
@@ -730,6 +758,12 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
   if (cfg.bm == 192 && cfg.bn == 256) return launch_cfg<192, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
+  if constexpr (MODE != kGateUpSilu && !Q) {
+    // column halves of the down projection's tail: the 192x256 and 256x256
+    // tiles' per-wave shapes on four waves
+    if (cfg.bm == 192 && cfg.bn == 128) return launch_cfg<192, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
+    if (cfg.bm == 256 && cfg.bn == 128) return launch_cfg<256, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -840,6 +874,23 @@ int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, i
   return (tiles * 2 <= slots && nk % 2 == 0 && nk / 2 >= 4) ? 2 : 1;
 }
 
+// Whether the down projection runs its last partial round as column halves
+// (a second launch): 192- and 256-row tiles fill a CU alone, so R whole
+// rounds plus a fraction f of one take R + 1 tile times; with f <= 1/2 the
+// leftover tiles split into at most one round of half-width tiles, about
+// R + 1/2 (measured efficiency of the halves aside). Each output element
+// still sums its whole contraction in the same order: the results are the
+// same bits. The kernels decide again from the routing's own tile count.
+bool pick_tail_split(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t H,
+                     int64_t max_tiles) {
+  if (cfg.bm < 192 || cfg.bn != 256 || H % 256 != 0) return false;
+  const int64_t n_tiles = H / 256;
+  if (max_tiles * n_tiles < kRound) return false;  // one launch never fills a round
+  const double rounds = expected_row_tiles(T, K, E, cfg.bm) * (double)n_tiles / kRound;
+  const double f = rounds - floor(rounds);
+  return rounds >= 1.0 && f > 0.0 && f <= 0.5;
+}
+
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm) {
   (void)n_slots;
   (void)H;
@@ -885,7 +936,7 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         const int32_t* num_tiles, const float* topk_weights, int64_t H,
                         int64_t I, int64_t E, int64_t K, int64_t max_tiles, float* y,
                         float* out, const float* b2, hipStream_t stream, int ksplit,
-                        int64_t n_slots, uint16_t* y16) {
+                        int64_t n_slots, uint16_t* y16, bool tail) {
   if (out && ksplit > 1) return hipErrorInvalidValue;  // atomic adds of partial sums
   if (y16 && (out || ksplit > 1)) return hipErrorInvalidValue;  // whole rows, rounded once
   GemmArgs a{};
@@ -907,9 +958,23 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   a.topk = (int32_t)K;
   a.max_tiles = (int32_t)max_tiles;
   a.n_tiles = (int)((H + cfg.bn - 1) / cfg.bn);
-  if (out) return dispatch<kDownAtomic, false>(cfg, a, stream);
-  if (y16) return dispatch<kDownSlotBf16, false>(cfg, a, stream);
-  return dispatch<kDownSlot, false>(cfg, a, stream);
+  auto run = [&](GemmCfg c, const GemmArgs& g) {
+    if (out) return dispatch<kDownAtomic, false>(c, g, stream);
+    if (y16) return dispatch<kDownSlotBf16, false>(c, g, stream);
+    return dispatch<kDownSlot, false>(c, g, stream);
+  };
+  if (!tail || ksplit != 1 || cfg.bm < 192 || cfg.bn != 256 || H % 256 != 0 ||
+      (int64_t)a.max_tiles * a.n_tiles < kRound)
+    return run(cfg, a);
+  // whole rounds of the chip (one 192- or 256-row tile per CU), then the
+  // rest as column halves
+  a.phase = 1;
+  a.rounds_of = kRound;
+  hipError_t st = run(cfg, a);
+  if (st != hipSuccess) return st;
+  a.phase = 2;
+  a.n_tiles = (int)(H / 128);
+  return run(GemmCfg{cfg.bm, 128}, a);
 }
 
 bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block) {

@@ -189,6 +189,7 @@ struct Layout {
   moe::GemmCfg g1{}, g2{};
   int ks2 = 1;  // contraction split of the down projection
   bool y16 = false;  // slot rows stored as bf16
+  bool tail = false;  // the down projection's last partial round as column halves
   int64_t cap = 0, max_tiles = 0, nblk = 0;
   bool widened = false;       // room for bf16 copies of FP8 weights (grouped path)
   size_t w1dq = 0, w2dq = 0;
@@ -229,6 +230,8 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   if (L.y16) L.ks2 = 1;  // bf16 rows are whole sums, rounded once
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
+  L.tail = L.ks2 == 1 && !(flags & (MOE_FLAG_NO_TAIL_SPLIT | MOE_FLAG_FP8_WEIGHTS)) &&
+           moe::pick_tail_split(L.g2, T, K, E, H, L.max_tiles);
   L.nblk = moe::route_blocks(n);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
@@ -356,6 +359,14 @@ int moe_y_bf16(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t f
   return make_layout(T, H, I, E, K, flags).y16 ? 1 : 0;
 }
 
+int moe_down_tail_split(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
+  const int rc = check_sizes(T, H, I, E, K);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return 0;
+  const Layout L = make_layout(T, H, I, E, K, flags);
+  return L.path == MOE_PATH_GROUPED && L.tail ? 1 : 0;
+}
+
 }  // extern "C"
 
 namespace {
@@ -469,7 +480,7 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                             K, L.max_tiles, nullptr, out, ep.b2, stream)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, E, K, L.max_tiles, nullptr, out,
-                                        ep.b2, stream);
+                                        ep.b2, stream, 1, 0, nullptr, L.tail);
       if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
     } else {
       float* y = L.y16 ? nullptr : at<float>(ws, L.y);
@@ -480,7 +491,7 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                             T * K, y16)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, E, K, L.max_tiles, y, nullptr,
-                                        nullptr, stream, L.ks2, T * K, y16);
+                                        nullptr, stream, L.ks2, T * K, y16, L.tail);
       if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
       st = L.y16 ? moe::launch_combine_bf16(y16, topk_weights, slot_of, topk_ids, E, T, H, K,
                                             ep.b2, out, stream)
