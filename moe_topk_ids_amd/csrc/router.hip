@@ -11,16 +11,20 @@
 // Layout: a group of G lanes owns one token, lane s of the group holds
 // experts EPL*s .. EPL*s+EPL-1 in registers (EPL 4 up to 64 experts, 8 up to
 // 128, else 16; G the smallest power of two with EPL*G >= E), so a wave
-// serves 64/G tokens (4 at E=128). Every reduction over the group uses DPP
-// moves inside a row of 16 lanes (cross-lane permutes through LDS only for
-// groups of 32 and 64 lanes, E > 256). Each of the K
-// rounds is a group-wide maximum of a 64-bit key: the logit in an
-// order-preserving integer encoding above the complement of the expert id,
-// so the largest logit wins and, among equal logits, the lowest id. Selection
-// compares the fp32 logits themselves (softmax is increasing), so the chosen
-// ids do not depend on how exp() rounds. The K weights are computed at the
-// end, choice k on lane k mod G of the group, and renormalised by a group
-// sum.
+// serves 64/G tokens (4 at E=128). Each lane first sorts its EPL experts by
+// logit, largest first, the lower id first among equal logits (a Batcher
+// odd-even merge network on a 64-bit key: the logit in an order-preserving
+// integer encoding above the complemented position). Each of the K rounds
+// is then a group-wide maximum of the lanes' heads (32-bit, DPP moves inside
+// a row of 16 lanes, cross-row permutes only for groups of 32 and 64 lanes)
+// and a ballot: the lowest lane whose head reaches it holds the winner (the
+// largest logit, ties to the lowest id, as lanes hold ascending ids) and
+// pops its head. Selection compares the fp32 logits themselves (softmax is
+// increasing), so the chosen ids do not depend on how exp() rounds. A lane's
+// chosen experts are the first ones of its sorted list, won in the rounds
+// its bit mask records; their weights are computed at the end: exp(l - max)
+// over the softmax denominator, or, renormalised, over the group's sum of the
+// chosen exps (the denominator cancels there and is not formed).
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -49,45 +53,57 @@ __device__ __forceinline__ uint32_t xchg(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
 
-// Group-wide combine of a value over aligned groups of G lanes; every lane
-// of the group ends with the result (the pairings are perfect matchings,
-// and both partners combine the same two values, so they agree bitwise):
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror,
-// then lanes 16 and 32 apart.
+// Group-wide combine of a 32-bit value over aligned groups of G lanes; every
+// lane of the group ends with the result (the pairings are perfect
+// matchings, and both partners combine the same two values, so they agree
+// bitwise): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror, then lanes 16 and 32 apart.
 template <int G, typename F>
-__device__ __forceinline__ uint64_t group_reduce_u64(uint64_t k, F&& pick) {
-  auto step = [&](auto ctrl) {
-    constexpr int C = decltype(ctrl)::value;
-    const uint32_t lo = xchg<C>((uint32_t)k), hi = xchg<C>((uint32_t)(k >> 32));
-    k = pick(k, ((uint64_t)hi << 32) | lo);
-  };
-  if constexpr (G >= 2) step(std::integral_constant<int, 0xB1>{});
-  if constexpr (G >= 4) step(std::integral_constant<int, 0x4E>{});
-  if constexpr (G >= 8) step(std::integral_constant<int, 0x141>{});
-  if constexpr (G >= 16) step(std::integral_constant<int, 0x140>{});
-  if constexpr (G >= 32) step(std::integral_constant<int, 16>{});
-  if constexpr (G >= 64) step(std::integral_constant<int, 32>{});
+__device__ __forceinline__ uint32_t group_reduce(uint32_t k, F&& pick) {
+  if constexpr (G >= 2) k = pick(k, xchg<0xB1>(k));
+  if constexpr (G >= 4) k = pick(k, xchg<0x4E>(k));
+  if constexpr (G >= 8) k = pick(k, xchg<0x141>(k));
+  if constexpr (G >= 16) k = pick(k, xchg<0x140>(k));
+  if constexpr (G >= 32) k = pick(k, xchg<16>(k));
+  if constexpr (G >= 64) k = pick(k, xchg<32>(k));
   return k;
 }
 
 template <int G>
-__device__ __forceinline__ float group_max_f32(float v) {
-  return __uint_as_float((uint32_t)group_reduce_u64<G>(
-      __float_as_uint(v),
-      [](uint64_t a, uint64_t b) {
-        return (uint64_t)__float_as_uint(fmaxf(__uint_as_float((uint32_t)a),
-                                               __uint_as_float((uint32_t)b)));
-      }));
+__device__ __forceinline__ float group_sum_f32(float v) {
+  return __uint_as_float(group_reduce<G>(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
-template <int G>
-__device__ __forceinline__ float group_sum_f32(float v) {
-  return __uint_as_float((uint32_t)group_reduce_u64<G>(
-      __float_as_uint(v),
-      [](uint64_t a, uint64_t b) {
-        return (uint64_t)__float_as_uint(__uint_as_float((uint32_t)a) +
-                                         __uint_as_float((uint32_t)b));
-      }));
+// Sorts the N composite keys (hi, lo) into descending order with Batcher's
+// odd-even merge network (N a power of two; the loops unroll to a fixed
+// list of compare-exchanges).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint32_t (&hi)[N], uint32_t (&lo)[N]) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+      for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+        for (int i = 0; i < k; ++i) {
+          const int a = i + j, b = i + j + k;
+          if (b < N && a / (2 * p) == b / (2 * p)) {
+            const uint64_t ka = ((uint64_t)hi[a] << 32) | lo[a];
+            const uint64_t kb = ((uint64_t)hi[b] << 32) | lo[b];
+            const bool sw = kb > ka;
+            const uint32_t h = hi[a], l = lo[a];
+            hi[a] = sw ? hi[b] : hi[a];
+            lo[a] = sw ? lo[b] : lo[a];
+            hi[b] = sw ? h : hi[b];
+            lo[b] = sw ? l : lo[b];
+          }
+        }
+      }
+    }
+  }
 }
 
 // G lanes per token, EPL logits per lane, at most KMAX choices, VEC: E a
@@ -97,6 +113,8 @@ __global__ __launch_bounds__(kThreads) void topk_softmax_kernel(
     const float* __restrict__ logits, int64_t T, int32_t E, int32_t K, int renormalize,
     float* __restrict__ weights, int32_t* __restrict__ ids) {
   constexpr int kTokensPerBlock = kThreads / G;
+  constexpr int kOut = EPL < KMAX ? EPL : KMAX;  // choices one lane can hold
+  const int lane = threadIdx.x & 63;
   const int sub = threadIdx.x % G;
   const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / G;
   const bool live_tok = t < T;
@@ -121,66 +139,79 @@ __global__ __launch_bounds__(kThreads) void topk_softmax_kernel(
     for (int j = 0; j < EPL; ++j) v[j] = (live_tok && e0 + j < E) ? row[e0 + j] : -INFINITY;
   }
 
-  // softmax: max, then the sum of exp(v - max) (lane terms in order, then
-  // the group tree)
-  float m = -INFINITY;
+  // this lane's experts sorted: logit order bits (0 past E, below every real
+  // key) above 255 - position (the lower id first among equal logits)
+  uint32_t hi[EPL], lo[EPL];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) m = fmaxf(m, v[j]);
-  m = group_max_f32<G>(m);
-  float d = 0.f;
+  for (int j = 0; j < EPL; ++j) {
+    hi[j] = (e0 + j < E) ? ordered_bits(v[j]) : 0u;
+    lo[j] = 255u - (uint32_t)j;
+  }
+  sort_desc<EPL>(hi, lo);
+  uint32_t shi[kOut], slo[kOut];  // the head of the sorted list, kept for the output
 #pragma unroll
-  for (int j = 0; j < EPL; ++j)
-    if (e0 + j < E) d += expf(v[j] - m);
-  d = group_sum_f32<G>(d);
+  for (int i = 0; i < kOut; ++i) {
+    shi[i] = hi[i];
+    slo[i] = lo[i];
+  }
 
-  // selection keys: order-preserving logit bits above the complemented id;
-  // 0 marks an expert already chosen or past E (below every real key)
-  uint32_t key_hi[EPL];
+  // K rounds: the group's largest head; the lowest lane holding it pops it
+  const int gbase = lane & ~(G - 1);
+  uint32_t won = 0;  // bit k: this lane won round k
+  uint32_t top = 0;  // the token's largest logit (order bits), round 0's maximum
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const uint32_t gmax =
+        group_reduce<G>(hi[0], [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    top = k == 0 ? gmax : top;
+    const uint64_t hit = __ballot(hi[0] == gmax);
+    int wsub;
+    if constexpr (G == 64) wsub = __builtin_ctzll(hit);
+    else wsub = __builtin_ctz((uint32_t)(hit >> gbase) & (uint32_t)((1ull << G) - 1));
+    // the owner pops its head: a bitwise select on an all-ones mask (kept
+    // opaque: as selects on `owner` the optimiser turns the shift into
+    // selects by a pop count, each a compare chain over the list)
+    uint32_t pop = sub == wsub ? ~0u : 0u;
+    asm volatile("" : "+v"(pop));
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) key_hi[j] = (e0 + j < E) ? ordered_bits(v[j]) : 0u;
+    for (int j = 0; j + 1 < EPL; ++j) hi[j] = (hi[j + 1] & pop) | (hi[j] & ~pop);
+    hi[EPL - 1] &= ~pop;
+    won |= pop & (1u << k);
+  }
 
-  // K rounds; every lane of the group learns each winner. Lane sub keeps the
-  // winners of rounds sub, sub + G, ... for the weights below.
-  constexpr int kMine = (KMAX + G - 1) / G;
-  uint64_t mine[kMine];
+  // weights: exp(l - max) of each chosen expert, over the softmax
+  // denominator (lane terms in order, then the group tree) or, renormalised,
+  // over the group's sum of the chosen exps
+  const float m = from_ordered_bits(top);
+  float den = 0.f;
+  if (!renormalize) {
 #pragma unroll
-  for (int r = 0; r < kMine; ++r) mine[r] = 0;
+    for (int j = 0; j < EPL; ++j)
+      if (e0 + j < E) den += expf(v[j] - m);
+    den = group_sum_f32<G>(den);
+  }
+  float x[kOut];
+  int r[kOut];
+  uint32_t rest = won;
+  float xsum = 0.f;
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    if (k < K) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const uint64_t key = ((uint64_t)key_hi[j] << 32) | (0xffffffffu - (uint32_t)(e0 + j));
-        best = (key_hi[j] != 0u && key > best) ? key : best;
-      }
-      best = group_reduce_u64<G>(best, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
-      const int jj = (int)(0xffffffffu - (uint32_t)best) - e0;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        if (j == jj) key_hi[j] = 0u;  // the owner lane removes the chosen expert
-      if (k % G == sub) mine[k / G] = best;
+  for (int i = 0; i < kOut; ++i) {
+    r[i] = -1;
+    x[i] = 0.f;
+    if (rest != 0u) {  // the lane's i-th choice, won in round r[i]
+      r[i] = __builtin_ctz(rest);
+      rest &= rest - 1u;
+      x[i] = expf(from_ordered_bits(shi[i]) - m);
+      xsum += x[i];
     }
   }
-
-  // weights: p = exp(logit - max) / denominator for each choice, on the lane
-  // that keeps it; the renormalising sum over the K choices is a group sum
-  float p[kMine];
-  float psum = 0.f;
-#pragma unroll
-  for (int r = 0; r < kMine; ++r) {
-    const int k = sub + G * r;
-    p[r] = k < K ? expf(from_ordered_bits((uint32_t)(mine[r] >> 32)) - m) / d : 0.f;
-    psum += p[r];
-  }
-  if (renormalize) psum = group_sum_f32<G>(psum);
+  if (renormalize) den = group_sum_f32<G>(xsum);
   if (live_tok) {
 #pragma unroll
-    for (int r = 0; r < kMine; ++r) {
-      const int k = sub + G * r;
-      if (k < K) {
-        weights[t * K + k] = renormalize ? p[r] / psum : p[r];
-        ids[t * K + k] = (int32_t)(0xffffffffu - (uint32_t)mine[r]);
+    for (int i = 0; i < kOut; ++i) {
+      if (r[i] >= 0) {
+        weights[t * K + r[i]] = x[i] / den;
+        ids[t * K + r[i]] = e0 + (int32_t)(255u - slo[i]);
       }
     }
   }
