@@ -881,14 +881,33 @@ int pick_ksplit(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles, i
 // R + 1/2 (measured efficiency of the halves aside). Each output element
 // still sums its whole contraction in the same order: the results are the
 // same bits. The kernels decide again from the routing's own tile count.
-bool pick_tail_split(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t H,
-                     int64_t max_tiles) {
-  if (cfg.bm < 192 || cfg.bn != 256 || H % 256 != 0) return false;
-  const int64_t n_tiles = H / 256;
+// n_rows: the weight rows per expert (H); kdim: the contraction (I). Only for
+// contractions of at least 16 stages: with fewer, a half-width tile pays a
+// whole tile's prologue and epilogue for half the work (measured slower on
+// the E=128, I=384 and I=768 rows). The same split of the gate/up product
+// measured slower on the E=128, I=768 rows and is not offered.
+// The tile count is estimated here as sum_j P(rows > j*bm) per expert under
+// the normal approximation of the binomial row count (the cost model's five
+// points misplace experts whose mean sits on a tile boundary, as at T=8192,
+// E=128: 512 rows per expert on 256-row tiles); if the routing's own count
+// leaves more than half a round, the kernels run it whole and the second
+// launch has nothing to do.
+bool pick_tail_split(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_rows,
+                     int64_t kdim, int64_t max_tiles) {
+  if (cfg.bm < 192 || cfg.bn != 256 || n_rows % 256 != 0 || kdim < 16 * 64) return false;
+  const int64_t n_tiles = n_rows / 256;
   if (max_tiles * n_tiles < kRound) return false;  // one launch never fills a round
-  const double rounds = expected_row_tiles(T, K, E, cfg.bm) * (double)n_tiles / kRound;
-  const double f = rounds - floor(rounds);
-  return rounds >= 1.0 && f > 0.0 && f <= 0.5;
+  const int64_t n = T * K;
+  const double live = (double)(n < E ? n : E);
+  const double mean = (double)n / live;
+  const double p = (double)K / (double)E;
+  const double sd = fmax(sqrt((double)T * p * (1.0 - p)), 1e-9);
+  double per_expert = 0.0;  // E[ceil(rows / bm)] for rows >= 1
+  for (int64_t j = 0; (double)j * cfg.bm < mean + 8.0 * sd; ++j)
+    per_expert += j == 0 ? 1.0 : 0.5 * erfc(((double)j * cfg.bm + 0.5 - mean) / (sd * sqrt(2.0)));
+  const double rounds = live * per_expert * (double)n_tiles / kRound;
+  const double f = rounds - floor(rounds);  // (a few hundredths: whole rounds but for rare experts)
+  return rounds >= 1.0 && f > 0.03 && f <= 0.5;
 }
 
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm) {

@@ -231,7 +231,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
   L.tail = L.ks2 == 1 && !(flags & (MOE_FLAG_NO_TAIL_SPLIT | MOE_FLAG_FP8_WEIGHTS)) &&
-           moe::pick_tail_split(L.g2, T, K, E, H, L.max_tiles);
+           moe::pick_tail_split(L.g2, T, K, E, H, I, L.max_tiles);
   L.nblk = moe::route_blocks(n);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);

@@ -91,8 +91,8 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
                         int64_t n_slots = 0, uint16_t* y16 = nullptr, bool tail = false);
 // tail: with ksplit 1, run a last partial round of at most half the chip as
 // column halves in a second launch (pick_tail_split; same results bit for bit).
-bool pick_tail_split(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t H,
-                     int64_t max_tiles);
+bool pick_tail_split(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_rows,
+                     int64_t kdim, int64_t max_tiles);
 
 // Split of the down projection's contraction (1 or 2; see gemm.hip):
 // with ksplit > 1, launch_gemm2 writes ksplit partial slot buffers y + s*n_slots*H.
