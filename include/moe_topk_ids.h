@@ -55,7 +55,7 @@ extern "C" {
 #define MOE_ERR_INVALID_ARG (-1) /* null pointer with T > 0, bad sizes, K > E, bad ids */
 #define MOE_ERR_UNSUPPORTED (-2) /* H or I not a multiple of 128, E > 1024, ... */
 #define MOE_ERR_HIP (-3)         /* a HIP runtime call failed */
-#define MOE_ERR_ALLOC (-4)       /* device allocation of the internal workspace failed */
+#define MOE_ERR_ALLOC (-4)       /* internal workspace: allocation failed or above MOE_WORKSPACE_LIMIT */
 #define MOE_ERR_WORKSPACE (-5)   /* caller workspace too small or misaligned */
 
 /* Combine the K expert outputs with fp32 atomic adds straight from the down
@@ -71,7 +71,11 @@ extern "C" {
  * expert's rows; meant for one or two tokens). */
 #define MOE_FLAG_FORCE_DECODE 4u
 /* Synchronise the stream after every stage and name the first stage whose
- * kernels failed in moe_last_error(). */
+ * kernels failed in moe_last_error(). The workspace layout then also holds a
+ * 256-byte guard band after every region (moe_workspace_bytes with this flag
+ * counts them), filled before the first stage and compared after each: a
+ * stage that wrote past its region returns MOE_ERR_WORKSPACE naming the
+ * stage and the region. */
 #define MOE_FLAG_DEBUG_SYNC 8u
 /* Check ids on the device; see the preconditions above. Synchronises. */
 #define MOE_FLAG_VALIDATE_IDS 16u
@@ -113,7 +117,9 @@ extern "C" {
  * workspace through moe_forward_ex. Two environment variables, read once
  * per process, set its flags: MOE_COMBINE ("slot", the default, or "atomic":
  * MOE_FLAG_ATOMIC_COMBINE) and MOE_DEBUG_SYNC (any value but "" or "0":
- * MOE_FLAG_DEBUG_SYNC).
+ * MOE_FLAG_DEBUG_SYNC). A third, MOE_WORKSPACE_LIMIT (bytes; unset or 0 for
+ * none), caps the internal workspace of every entry point that uses it: a
+ * call that would need more returns MOE_ERR_ALLOC before any device work.
  */
 int moe_forward(const void* hidden, const void* w1, const void* w2,
                 const float* topk_weights, const int32_t* topk_ids,

@@ -195,28 +195,43 @@ struct Layout {
   size_t w1dq = 0, w2dq = 0;
   size_t err = 0, counts = 0, offsets = 0, num_tiles = 0, tile_expert = 0, sorted = 0,
          slot_of = 0, block_hist = 0, act = 0, y = 0, total = 0;
+  // MOE_FLAG_DEBUG_SYNC: a guard band of kGuardBytes after every region,
+  // filled before the first stage and checked after each one
+  static constexpr int kMaxGuards = 16;
+  int n_guards = 0;
+  size_t guard[kMaxGuards] = {};
+  const char* guard_after[kMaxGuards] = {};
 };
+
+constexpr size_t kGuardBytes = 256;
+constexpr unsigned char kGuardByte = 0xA5;
 
 Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t flags) {
   Layout L;
   const int64_t n = T * K;
   size_t p = 0;
-  auto take = [&](size_t bytes) {
+  const bool guarded = (flags & MOE_FLAG_DEBUG_SYNC) != 0;
+  auto take = [&](size_t bytes, const char* name) {
     const size_t at = p;
     p = align_up(p + bytes);
+    if (guarded && L.n_guards < Layout::kMaxGuards) {
+      L.guard[L.n_guards] = p;
+      L.guard_after[L.n_guards++] = name;
+      p += kGuardBytes;
+    }
     return at;
   };
-  L.err = take(sizeof(int32_t));
+  L.err = take(sizeof(int32_t), "error flag");
   L.path = pick_path(T, H, I, E, K, flags);
   if (L.path == MOE_PATH_DECODE) {
     L.decode = true;
-    L.act = take((size_t)n * I * 2);
+    L.act = take((size_t)n * I * 2, "act");
     L.total = p;
     return L;
   }
   if (L.path == MOE_PATH_SMALL_BATCH) {
-    L.act = take((size_t)n * I * 2);
-    L.y = take((size_t)n * H * 4);
+    L.act = take((size_t)n * I * 2, "act");
+    L.y = take((size_t)n * H * 4, "slot rows");
     L.total = p;
     return L;
   }
@@ -233,19 +248,20 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
   L.tail = L.ks2 == 1 && !(flags & (MOE_FLAG_NO_TAIL_SPLIT | MOE_FLAG_FP8_WEIGHTS)) &&
            moe::pick_tail_split(L.g2, T, K, E, H, I, L.max_tiles);
   L.nblk = moe::route_blocks(n);
-  L.counts = take((size_t)E * 4);
-  L.offsets = take((size_t)(E + 1) * 4);
-  L.num_tiles = take(4);
-  L.tile_expert = take((size_t)L.max_tiles * 4);
-  L.sorted = take((size_t)L.cap * 4);
-  L.slot_of = take((size_t)n * 4);
-  L.block_hist = take((size_t)E * L.nblk * 4);
-  L.act = take((size_t)L.cap * I * 2);
-  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) L.y = take((size_t)L.ks2 * n * H * (L.y16 ? 2 : 4));
+  L.counts = take((size_t)E * 4, "counts");
+  L.offsets = take((size_t)(E + 1) * 4, "offsets");
+  L.num_tiles = take(4, "num_tiles");
+  L.tile_expert = take((size_t)L.max_tiles * 4, "tile_expert");
+  L.sorted = take((size_t)L.cap * 4, "sorted");
+  L.slot_of = take((size_t)n * 4, "slot_of");
+  L.block_hist = take((size_t)E * L.nblk * 4, "block histograms");
+  L.act = take((size_t)L.cap * I * 2, "act");
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE))
+    L.y = take((size_t)L.ks2 * n * H * (L.y16 ? 2 : 4), "slot rows");
   if ((flags & MOE_FLAG_FP8_WEIGHTS) && fp8_may_widen(T, H, I, E, K)) {
     L.widened = true;
-    L.w1dq = take((size_t)E * 2 * I * H * 2);
-    L.w2dq = take((size_t)E * H * I * 2);
+    L.w1dq = take((size_t)E * 2 * I * H * 2, "widened w1");
+    L.w2dq = take((size_t)E * H * I * 2, "widened w2");
   }
   L.total = p;
   return L;
@@ -302,12 +318,56 @@ uint32_t env_flags() {
   return flags;
 }
 
-int stage_check(uint32_t flags, const char* stage, hipError_t launch, hipStream_t stream) {
+// Largest internal workspace the library may allocate, read once from the
+// environment (MOE_WORKSPACE_LIMIT, bytes; unset or 0: no limit).
+size_t workspace_limit() {
+  static size_t limit = [] {
+    const char* v = std::getenv("MOE_WORKSPACE_LIMIT");
+    return v ? (size_t)std::strtoull(v, nullptr, 10) : (size_t)0;
+  }();
+  return limit;
+}
+
+// MOE_FLAG_DEBUG_SYNC: the guard bands of the layout (see Layout), set
+// before the first stage and compared after each.
+struct Guards {
+  const Layout* L = nullptr;
+  void* ws = nullptr;
+};
+
+int fill_guards(const Layout& L, void* ws, hipStream_t stream) {
+  for (int i = 0; i < L.n_guards; ++i) {
+    hipError_t st = hipMemsetAsync(static_cast<char*>(ws) + L.guard[i], kGuardByte, kGuardBytes,
+                                   stream);
+    if (st != hipSuccess) return hip_error("workspace guard fill", st);
+  }
+  return MOE_OK;
+}
+
+int check_guards(const Guards& g, const char* stage) {
+  if (!g.L) return MOE_OK;
+  unsigned char buf[kGuardBytes];
+  for (int i = 0; i < g.L->n_guards; ++i) {
+    hipError_t st = hipMemcpy(buf, static_cast<char*>(g.ws) + g.L->guard[i], kGuardBytes,
+                              hipMemcpyDeviceToHost);
+    if (st != hipSuccess) return hip_error("workspace guard check", st);
+    for (size_t b = 0; b < kGuardBytes; ++b)
+      if (buf[b] != kGuardByte)
+        return set_error(MOE_ERR_WORKSPACE,
+                         "stage %s wrote past the workspace region '%s' (guard byte %zu is 0x%02x)",
+                         stage, g.L->guard_after[i], b, buf[b]);
+  }
+  return MOE_OK;
+}
+
+int stage_check(uint32_t flags, const char* stage, hipError_t launch, hipStream_t stream,
+                const Guards& guards = Guards{}) {
   if (launch != hipSuccess) return hip_error(stage, launch);
   if (flags & MOE_FLAG_DEBUG_SYNC) {
     hipError_t st = hipStreamSynchronize(stream);
     if (st == hipSuccess) st = hipGetLastError();
     if (st != hipSuccess) return set_error(MOE_ERR_HIP, "stage %s failed: %s", stage, hipGetErrorString(st));
+    return check_guards(guards, stage);
   }
   return MOE_OK;
 }
@@ -411,10 +471,21 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
     if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
       return set_error(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   } else {
+    const size_t limit = workspace_limit();
+    if (limit && L.total > limit)
+      return set_error(MOE_ERR_ALLOC,
+                       "the internal workspace would need %zu bytes, above MOE_WORKSPACE_LIMIT=%zu",
+                       L.total, limit);
     rc = internal_workspace(L.total, &ws);
     if (rc != MOE_OK) return rc;
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  Guards gd;
+  if (L.n_guards) {
+    if ((rc = fill_guards(L, ws, stream)) != MOE_OK) return rc;
+    gd.L = &L;
+    gd.ws = ws;
+  }
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* wa = static_cast<const uint16_t*>(w1);
   const auto* wb = static_cast<const uint16_t*>(w2);
@@ -423,7 +494,7 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
   if (validate) {
     hipError_t st = hipMemsetAsync(err, 0, sizeof(int32_t), stream);
     if (st == hipSuccess) st = moe::launch_validate_ids(topk_ids, T, K, E, err, stream);
-    if ((rc = stage_check(flags, "validate_ids", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "validate_ids", st, stream, gd)) != MOE_OK) return rc;
   }
 
   if (L.decode) {
@@ -432,7 +503,7 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                    at<uint16_t>(ws, L.act), out, ep, stream)
           : moe::launch_decode(x, wa, wb, topk_weights, topk_ids, T, H, I, E, K,
                                at<uint16_t>(ws, L.act), out, ep, stream);
-    if ((rc = stage_check(flags, "decode", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "decode", st, stream, gd)) != MOE_OK) return rc;
   } else if (L.path == MOE_PATH_SMALL_BATCH) {
     float* y = at<float>(ws, L.y);
     hipError_t st =
@@ -440,9 +511,9 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                                         y, ep, stream)
           : moe::launch_small_batch(x, wa, wb, topk_ids, T, H, I, E, K, at<uint16_t>(ws, L.act),
                                     y, ep, stream);
-    if ((rc = stage_check(flags, "small_batch", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "small_batch", st, stream, gd)) != MOE_OK) return rc;
     st = moe::launch_combine(y, topk_weights, nullptr, topk_ids, E, T, H, K, ep.b2, out, stream);
-    if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "combine", st, stream, gd)) != MOE_OK) return rc;
   } else {
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -459,29 +530,29 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
         return set_error(MOE_ERR_UNSUPPORTED, "no room for the widened FP8 weights");
       st = moe::launch_dequant_fp8(*q, E, H, I, at<uint16_t>(ws, L.w1dq),
                                    at<uint16_t>(ws, L.w2dq), stream);
-      if ((rc = stage_check(flags, "dequant_fp8", st, stream)) != MOE_OK) return rc;
+      if ((rc = stage_check(flags, "dequant_fp8", st, stream, gd)) != MOE_OK) return rc;
       wa = at<uint16_t>(ws, L.w1dq);
       wb = at<uint16_t>(ws, L.w2dq);
     }
     st = moe::launch_route(topk_ids, T, K, E, L.g1.bm, block_hist, counts, offsets,
                                       sorted, slot_of, tile_expert, num_tiles, stream);
-    if ((rc = stage_check(flags, "route", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "route", st, stream, gd)) != MOE_OK) return rc;
     st = q_native ? moe::launch_gemm1_silu_fp8(L.g1, x, q->w1q, q->w1s, q->block, sorted,
                                                tile_expert, num_tiles, T, H, I, E, K,
                                                L.max_tiles, act, ep, stream)
                   : moe::launch_gemm1_silu(L.g1, x, wa, sorted, tile_expert, num_tiles, T, H, I,
                                            E, K, L.max_tiles, act, ep, stream);
-    if ((rc = stage_check(flags, "gemm1_silu", st, stream)) != MOE_OK) return rc;
+    if ((rc = stage_check(flags, "gemm1_silu", st, stream, gd)) != MOE_OK) return rc;
     if (flags & MOE_FLAG_ATOMIC_COMBINE) {
       st = moe::launch_zero(out, T * H, stream);
-      if ((rc = stage_check(flags, "zero_out", st, stream)) != MOE_OK) return rc;
+      if ((rc = stage_check(flags, "zero_out", st, stream, gd)) != MOE_OK) return rc;
       st = q_native ? moe::launch_gemm2_fp8(L.g2, act, q->w2q, q->w2s, q->block, sorted,
                                             tile_expert, num_tiles, topk_weights, H, I, E,
                                             K, L.max_tiles, nullptr, out, ep.b2, stream)
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, E, K, L.max_tiles, nullptr, out,
                                         ep.b2, stream, 1, 0, nullptr, L.tail);
-      if ((rc = stage_check(flags, "gemm2_atomic", st, stream)) != MOE_OK) return rc;
+      if ((rc = stage_check(flags, "gemm2_atomic", st, stream, gd)) != MOE_OK) return rc;
     } else {
       float* y = L.y16 ? nullptr : at<float>(ws, L.y);
       uint16_t* y16 = L.y16 ? at<uint16_t>(ws, L.y) : nullptr;
@@ -492,12 +563,12 @@ int forward_impl(const void* hidden, const void* w1, const void* w2, const moe::
                     : moe::launch_gemm2(L.g2, act, wb, sorted, tile_expert, num_tiles,
                                         topk_weights, H, I, E, K, L.max_tiles, y, nullptr,
                                         nullptr, stream, L.ks2, T * K, y16, L.tail);
-      if ((rc = stage_check(flags, "gemm2_slot", st, stream)) != MOE_OK) return rc;
+      if ((rc = stage_check(flags, "gemm2_slot", st, stream, gd)) != MOE_OK) return rc;
       st = L.y16 ? moe::launch_combine_bf16(y16, topk_weights, slot_of, topk_ids, E, T, H, K,
                                             ep.b2, out, stream)
                  : moe::launch_combine(y, topk_weights, slot_of, topk_ids, E, T, H, K, ep.b2,
                                        out, stream, L.ks2);
-      if ((rc = stage_check(flags, "combine", st, stream)) != MOE_OK) return rc;
+      if ((rc = stage_check(flags, "combine", st, stream, gd)) != MOE_OK) return rc;
     }
   }
 

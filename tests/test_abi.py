@@ -211,3 +211,41 @@ def test_noalloc_rejects_sizes_beyond_its_array_on_the_host(lib):
         moe.MOE_ERR_INVALID_ARG
     # prefill's workspace fits the array
     assert 0 < lib.moe_workspace_bytes(4195, 2048, 2048, 8, 2, 0) <= moe.NOALLOC_SCRATCH_BYTES
+
+
+def test_workspace_limit_gives_alloc_error_before_any_device_work():
+    """MOE_WORKSPACE_LIMIT caps the internal workspace: a call that would need
+    more returns MOE_ERR_ALLOC, and does so before any HIP call (this runs
+    without a GPU); a call with its own workspace is not limited (it then
+    reaches the device and fails differently here)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, moe_topk_ids_amd as moe\n"
+        "lib = moe.load_library()\n"
+        "p = ctypes.c_void_p(256)\n"
+        "rc = lib.moe_forward_ex(p, p, p, p, p, 4195, 2048, 2048, 8, 2, p, 0, None, 0, None)\n"
+        "print(rc, lib.moe_last_error().decode())\n"
+        "need = lib.moe_workspace_bytes(4195, 2048, 2048, 8, 2, 0)\n"
+        "rc2 = lib.moe_forward_ex(p, p, p, p, p, 4195, 2048, 2048, 8, 2, p, 0, p, need, None)\n"
+        "print(rc2)\n")
+    env = dict(os.environ, MOE_WORKSPACE_LIMIT="4096")
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    first, second = r.stdout.strip().splitlines()[-2:]
+    rc, msg = first.split(" ", 1)
+    assert int(rc) == moe.MOE_ERR_ALLOC
+    assert "MOE_WORKSPACE_LIMIT=4096" in msg
+    assert int(second) != moe.MOE_ERR_ALLOC
+
+
+def test_debug_sync_layout_holds_guard_bands(lib):
+    """With MOE_FLAG_DEBUG_SYNC the workspace layout places a 256-byte guard
+    band after every region: the size grows by whole bands on every path."""
+    for shape, regions in (((4195, 2048, 2048, 8, 2), 10),  # grouped: 10 regions
+                           ((1, 2048, 768, 128, 8), 2),     # per token: error flag, act
+                           ((40, 2048, 768, 128, 8), 3)):   # small batch: + slot rows
+        plain = lib.moe_workspace_bytes(*shape, 0)
+        guarded = lib.moe_workspace_bytes(*shape, moe.FLAG_DEBUG_SYNC)
+        assert guarded - plain == regions * 256, shape

@@ -413,11 +413,20 @@ def test_decode_tokens_are_independent(shape):
                  f"decode-two-tokens/{shape}")
 
 
-def test_debug_sync_flag():
+@pytest.mark.parametrize("name,path", [
+    ("tiny", "slot"), ("prefill", "slot"), ("prefill", "atomic"), ("decode", "decode"),
+    ("tiny", "small_batch"),
+])
+def test_debug_sync_flag(name, path):
+    """MOE_FLAG_DEBUG_SYNC (a synchronisation and a check of the workspace
+    guard bands after every stage) leaves the results' bits unchanged, and no
+    stage writes past its workspace region on any path (prefill takes the
+    down projection's tail launch)."""
     require_gpu()
-    dd = to_device(shape_inputs("tiny"))
-    a = _run(dd, PATHS["slot"] | moe.FLAG_DEBUG_SYNC)
-    b = _run(dd, PATHS["slot"])
+    dd = to_device(shape_inputs(name))
+    say(f"debug sync {name} {path}")
+    a = _run(dd, PATHS[path] | moe.FLAG_DEBUG_SYNC)
+    b = _run(dd, PATHS[path])
     assert np.array_equal(a, b)
 
 
