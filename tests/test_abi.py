@@ -249,3 +249,19 @@ def test_debug_sync_layout_holds_guard_bands(lib):
         plain = lib.moe_workspace_bytes(*shape, 0)
         guarded = lib.moe_workspace_bytes(*shape, moe.FLAG_DEBUG_SYNC)
         assert guarded - plain == regions * 256, shape
+
+
+def test_tail_split_plan(lib):
+    """The down projection's column-half tail launch is planned for the prefill
+    shape (384 tiles of 192x256: 1.5 rounds) and T=8179, H=I=4096 (~4.2
+    rounds), not where its contraction is short (I=384: 6 stages), not with
+    FP8 weights, not with MOE_FLAG_NO_TAIL_SPLIT, and not on the streaming
+    paths."""
+    assert moe.moe_down_tail_split(4195, 2048, 2048, 8, 2, 0)
+    assert moe.moe_down_tail_split(8179, 4096, 4096, 8, 2, 0)
+    assert not moe.moe_down_tail_split(3936, 4096, 384, 128, 8, 0)
+    assert not moe.moe_down_tail_split(4195, 2048, 2048, 8, 2, moe.FLAG_FP8_WEIGHTS)
+    assert not moe.moe_down_tail_split(4195, 2048, 2048, 8, 2, moe.FLAG_NO_TAIL_SPLIT)
+    assert not moe.moe_down_tail_split(1, 2048, 768, 128, 8, 0)
+    assert not moe.moe_down_tail_split(15381, 4096, 4096, 8, 2, 0)  # whole rounds
+    assert lib.moe_down_tail_split(4, 100, 128, 8, 2, 0) == moe.MOE_ERR_UNSUPPORTED

@@ -292,6 +292,41 @@ def test_all_tokens_one_expert_and_empty_experts():
                      f"one-expert/{path}")
 
 
+@pytest.mark.parametrize("T,H,I,E,K,skew", [
+    (2000, 1024, 1024, 64, 2, "two_hot"),   # 90 % of the slots on experts 0 and 1
+    (5000, 2048, 1024, 32, 4, "same_four"),  # every token on experts 0..3
+    (1500, 512, 512, 128, 8, "zipf"),        # expert e drawn with weight 1 / (e + 1)
+])
+def test_skewed_routing_live_tiles(T, H, I, E, K, skew):
+    """The grouped GEMMs size their grid for every row tile the routing could
+    produce and number only the live ones: with skewed routings (few live
+    tiles against that bound, partial tile windows) every tile is computed
+    exactly once on the slot and atomic paths (a tile taken twice would be
+    added twice on the atomic path)."""
+    require_gpu()
+    d = dict(cpu_inputs(T, H, I, E, K, seed=T + K))
+    rng = np.random.default_rng(T)
+    if skew == "two_hot":
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        hot = rng.random(T) < 0.9
+        ids[hot] = np.array([0, 1])
+    elif skew == "same_four":
+        ids = np.tile(np.arange(K), (T, 1))
+    else:
+        p = 1.0 / np.arange(1, E + 1)
+        ids = np.stack([rng.choice(E, size=K, replace=False, p=p / p.sum()) for _ in range(T)])
+    d["topk_ids"] = torch.from_numpy(ids.astype(np.int32))
+    dd = to_device(d)
+    rows = sample_rows(T, 256, seed=4)
+    want = oracle_rows(d, rows)
+    for path in ("slot", "atomic"):
+        for extra in (0, moe.FLAG_NO_TAIL_SPLIT):
+            say(f"skewed {skew} T={T} E={E} K={K} {path} extra={extra}")
+            got = _run(dd, PATHS[path] | extra)
+            assert_close(got[rows], want, tight_rows(d, rows, PATHS[path]),
+                         f"skewed-{skew}/{path}")
+
+
 def test_out_of_range_ids_are_dropped():
     require_gpu()
     d = dict(cpu_inputs(64, 512, 256, 8, 2, seed=6))
