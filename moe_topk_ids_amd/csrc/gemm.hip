@@ -193,7 +193,13 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
     // the tile's intermediate: BM rows x BN/2 bf16 columns; with STAGED it
     // leaves through LDS (see the bf16 slot rows below)
     constexpr int CPRO = BN / 16;  // 16-byte chunks per staged row
-    if constexpr (STAGED) __syncthreads();  // every wave is done with the last stage
+    if constexpr (STAGED) {
+      // every load of this wave has landed (the last step issues one stage
+      // past the end, whose zeros go to the ring the tile is staged in) and
+      // every wave is done with the last stage
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
     // v: columns col + 8j .. col + 8j + 3 of token row r (tile row tm*32 +
     // (lane & 31) of the wave, sub-tile tn)
     auto emit = [&](int64_t r, int64_t col, int tm, int tn, int j, uint2 v) {
@@ -310,6 +316,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& args,
     constexpr int ITERS = BM / RPI / NWE;
     static_assert(64 % CPRO == 0 && (BM / RPI) % NWE == 0, "staged output rows");
     const int wave = wn * (BM / WTM) + wm;
+    wait_vmcnt<0>();  // (as above: the past-the-end stage's zeros have landed)
     __syncthreads();
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
