@@ -57,6 +57,35 @@ def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:
     return np.sort(np.concatenate([[0, T - 1], mid]))
 
 
+def random_shapes(n: int, seed: int):
+    """Seeded shapes spread over the library's choices, a third each of:
+    1-8 tokens (per-token and per-expert paths), 9-399 tokens (grouped, few
+    rows per expert) and 1000-8999 tokens over at most 16 experts (grouped,
+    the 192- and 256-row tiles and the down projection's tail). Top-1 to
+    top-8; H and I any multiple of 128 up to 2048 and 1536 (at least 512 in
+    the last third). Expert weights stay at most 2^25 elements per matrix, so
+    the inputs are drawn and checked in about a second."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        band = len(shapes) % 3
+        if band < 2:
+            E = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32, 60, 64, 128, 200, 256]))
+            T = int(rng.integers(1, 9) if band == 0 else rng.integers(9, 400))
+            H = 128 * int(rng.integers(1, 17))
+            I = 128 * int(rng.integers(1, 13))
+        else:
+            E = int(rng.choice([1, 2, 3, 4, 8, 16]))
+            T = int(rng.integers(1000, 9000))
+            H = 128 * int(rng.integers(4, 17))
+            I = 128 * int(rng.integers(4, 13))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        if E * I * H > 1 << 25:
+            continue
+        shapes.append((T, H, I, E, K))
+    return shapes
+
+
 def oracle_rows(d: dict, rows: np.ndarray, bf16_inter: bool = False,
                 bf16_y: bool = False) -> np.ndarray:
     """The oracle's output for a subset of token rows (each row of the

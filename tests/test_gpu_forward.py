@@ -5,9 +5,9 @@ import torch
 
 import moe_topk_ids_amd as moe
 import oracle
-from gpu_helpers import (REL_L2_BF16_INTER, assert_close, cpu_inputs, oracle_rows, rel_l2,
-                         require_gpu, sample_rows, say, shape_inputs, tight_rows, to_device,
-                         y_bf16_for)
+from gpu_helpers import (REL_L2_BF16_INTER, assert_close, cpu_inputs, oracle_rows,
+                         random_shapes, rel_l2, require_gpu, sample_rows, say, shape_inputs,
+                         tight_rows, to_device, y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, Shape, bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -277,36 +277,7 @@ def test_ragged_and_degenerate_shapes(T, H, I, E, K, path):
                  f"{T},{H},{I},{E},{K}/{path}")
 
 
-def _random_shapes(n: int, seed: int):
-    """Seeded shapes spread over the library's choices, a third each of:
-    1-8 tokens (per-token and per-expert paths), 9-399 tokens (grouped, few
-    rows per expert) and 1000-8999 tokens over at most 16 experts (grouped,
-    the 192- and 256-row tiles and the down projection's tail). Top-1 to
-    top-8; H and I any multiple of 128 up to 2048 and 1536 (at least 512 in
-    the last third). Expert weights stay at most 2^25 elements per matrix, so
-    the inputs are drawn and checked in about a second."""
-    rng = np.random.default_rng(seed)
-    shapes = []
-    while len(shapes) < n:
-        band = len(shapes) % 3
-        if band < 2:
-            E = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32, 60, 64, 128, 200, 256]))
-            T = int(rng.integers(1, 9) if band == 0 else rng.integers(9, 400))
-            H = 128 * int(rng.integers(1, 17))
-            I = 128 * int(rng.integers(1, 13))
-        else:
-            E = int(rng.choice([1, 2, 3, 4, 8, 16]))
-            T = int(rng.integers(1000, 9000))
-            H = 128 * int(rng.integers(4, 17))
-            I = 128 * int(rng.integers(4, 13))
-        K = int(rng.integers(1, min(E, 8) + 1))
-        if E * I * H > 1 << 25:
-            continue
-        shapes.append((T, H, I, E, K))
-    return shapes
-
-
-RANDOM_SHAPES = _random_shapes(24, seed=20261203)
+RANDOM_SHAPES = random_shapes(24, seed=20261203)
 
 
 @pytest.mark.parametrize("path", ["default", "slot"])

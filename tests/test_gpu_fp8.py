@@ -7,8 +7,8 @@ import torch
 
 import moe_topk_ids_amd as moe
 import oracle
-from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, rel_l2, require_gpu,
-                         sample_rows, say, shape_inputs, to_device, y_bf16_for)
+from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, random_shapes, rel_l2,
+                         require_gpu, sample_rows, say, shape_inputs, to_device, y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_biases, make_fp8_weights
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,39 @@ def test_fp8_on_every_path(path, act, kw, bias, block):
     tight = (_oracle(d, q, rows, okw, b, True) if path in ("decode", "small_batch")
              else _oracle_widened(d, q, rows, okw, b, PATHS[path]))
     _check(got, want, tight, f"fp8/{act}/bias={bias}/block={block}/{path}")
+
+
+# seeded shapes over every route and row tile (a different draw from the bf16
+# sweep), each with one of the activations, biases on every other shape, and
+# scale blocks of 128 or 256 where 256 divides H and I
+RANDOM_SHAPES = random_shapes(12, seed=20261204)
+RANDOM_ACTS = [("silu", {}), ("gelu_tanh", {}), ("swigluoai", {"alpha": 1.702, "limit": 0.1}),
+               ("gelu_erf", {})]
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM_SHAPES)))
+def test_fp8_and_variants_on_random_shapes(idx):
+    require_gpu()
+    T, H, I, E, K = RANDOM_SHAPES[idx]
+    act, kw = RANDOM_ACTS[idx % len(RANDOM_ACTS)]
+    block = 256 if idx % 3 == 0 and H % 256 == 0 and I % 256 == 0 else 128
+    d = cpu_inputs(T, H, I, E, K, seed=100 + idx)
+    q = make_fp8_weights(d, block)
+    b = make_biases(H, I, E, seed=100 + idx) if idx % 2 else None
+    dd, qd = to_device(d), _to_dev(q)
+    bd = None if b is None else to_device(b)
+    route = moe.moe_path(T, H, I, E, K, moe.FLAG_FP8_WEIGHTS)
+    say(f"fp8 random shape {idx}: T={T} H={H} I={I} E={E} K={K} act={act} bias={b is not None} "
+        f"block={block} route={route}")
+    kw = dict(kw, activation=act)
+    okw = {k: v for k, v in kw.items() if k != "activation"}
+    okw["act"] = act
+    got = _run(dd, qd, None, kw, bd)
+    rows = sample_rows(T, 32, seed=idx)
+    want = _oracle(d, q, rows, okw, b)
+    tight = (_oracle(d, q, rows, okw, b, True) if route != moe.PATH_GROUPED
+             else _oracle_widened(d, q, rows, okw, b, None))
+    _check(got[rows], want, tight, f"fp8 random {idx} {T},{H},{I},{E},{K}/{act}")
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill", "wide"])
