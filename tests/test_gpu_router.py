@@ -93,6 +93,33 @@ def test_router_edge_cases(T, E, K, kind):
     _check(logits, K, f"{kind}")
 
 
+def _random_router_cases(n: int, seed: int):
+    """Seeded (T, E, K, kind): expert counts on both sides of every layout
+    boundary of the kernel (4, 8 or 16 logits per lane; 1 to 64 lanes per
+    token; E a multiple of the lanes' vector width or not), top-1 to top-32,
+    1 to 5000 tokens, half of them with many exact ties."""
+    rng = np.random.default_rng(seed)
+    es = [2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 96, 127, 128, 129, 200, 255, 256,
+          257, 384, 511, 512, 513, 700, 1023, 1024]
+    cases = []
+    for i in range(n):
+        E = int(es[i % len(es)])
+        K = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.integers(1, 5000))
+        cases.append((T, E, K, "ties" if i % 2 else "normal"))
+    return cases
+
+
+@pytest.mark.parametrize("T,E,K,kind", _random_router_cases(30, seed=20261205))
+def test_router_random_cases(T, E, K, kind):
+    require_gpu()
+    rng = np.random.default_rng(T * 31 + E * 7 + K)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":
+        logits = np.round(logits * 2) / 2
+    _check(logits, K, f"random {kind}")
+
+
 def test_router_then_forward():
     """Logits -> GPU router -> GPU forward equals logits -> oracle router ->
     oracle forward, on the tiny workload."""
