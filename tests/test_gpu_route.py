@@ -104,3 +104,43 @@ def test_route_is_deterministic():
     tiles = int(a["num_tiles"].item())
     assert torch.equal(a["sorted"][:rows], b["sorted"][:rows])
     assert torch.equal(a["tile_expert"][:tiles], b["tile_expert"][:tiles])
+
+
+def _random_route_cases(n: int, seed: int):
+    """Seeded (T, K, E, M, kind): slot counts on both sides of the
+    single-workgroup limit (16384 slots) and up to 120,000 slots, 1 to 1024
+    experts, top-1 to top-8, every multiple of 16 for the row tile, and id
+    distributions uniform, skewed (Zipf-like expert popularity), or
+    concentrated on two experts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 8, 16, 60, 128, 256, 513, 1024]))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        slots = int(rng.choice([rng.integers(1, 300), rng.integers(300, 16385),
+                                rng.integers(16385, 120000)]))
+        T = max(1, slots // K)
+        M = 16 * int(rng.integers(1, 17))
+        cases.append((T, K, E, M, ["uniform", "skewed", "two_experts"][i % 3]))
+    return cases
+
+
+@pytest.mark.parametrize("T,K,E,M,kind", _random_route_cases(24, seed=20261206))
+def test_route_random_cases(T, K, E, M, kind):
+    require_gpu()
+    rng = np.random.default_rng(T + 13 * E + 7 * M)
+    if kind == "uniform" or E <= K:
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    else:
+        # distinct experts per token, drawn without replacement from a skewed
+        # popularity (kind "skewed": weight 1/(rank+1); "two_experts": nearly
+        # everything on experts 0 and 1)
+        if kind == "skewed":
+            p = 1.0 / (np.arange(E) + 1.0)
+        else:
+            p = np.full(E, 1e-3)
+            p[:2] = 1.0
+        p = p / p.sum()
+        ids = np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(T)]).astype(
+            np.int32)
+    _check_route(ids, E, M, f"random {kind}")
