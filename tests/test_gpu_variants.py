@@ -7,8 +7,8 @@ import torch
 
 import moe_topk_ids_amd as moe
 import oracle
-from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, rel_l2, require_gpu,
-                         sample_rows, say, shape_inputs, to_device, y_bf16_for)
+from gpu_helpers import (MAX_ABS, REL_L2, REL_L2_BF16_INTER, cpu_inputs, random_shapes, rel_l2,
+                         require_gpu, sample_rows, say, shape_inputs, to_device, y_bf16_for)
 from moe_topk_ids_amd.inputs import SHAPES, bf16_bits, make_biases
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,31 @@ def test_variant_at_workload_size(name, act, kw):
     rows = sample_rows(s.T, 256, seed=4)
     _check(got[rows], _oracle(d, rows, act, kw, b),
            _oracle(d, rows, act, kw, b, True, y_bf16_for(d, None)), f"{name}/{act}")
+
+
+# seeded shapes over every route and row tile (a third draw), each with the
+# next activation in turn and biases on every other shape; half of them on
+# the default route, half forced grouped
+RANDOM_SHAPES = random_shapes(15, seed=20261207)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM_SHAPES)))
+def test_variants_on_random_shapes(idx):
+    require_gpu()
+    T, H, I, E, K = RANDOM_SHAPES[idx]
+    act, kw = ACTS[idx % len(ACTS)]
+    d = cpu_inputs(T, H, I, E, K, seed=200 + idx)
+    b = make_biases(H, I, E, seed=200 + idx) if idx % 2 else None
+    dd = to_device(d)
+    bd = None if b is None else to_device(b)
+    fl = PATHS["slot"] if idx % 4 >= 2 else None
+    say(f"variant random shape {idx}: T={T} H={H} I={I} E={E} K={K} act={act}{kw} "
+        f"bias={b is not None} route={moe.moe_path(T, H, I, E, K, fl or 0)}")
+    got = _run(dd, fl, act, kw, bd)
+    rows = sample_rows(T, 32, seed=idx)
+    _check(got[rows], _oracle(d, rows, act, kw, b),
+           _oracle(d, rows, act, kw, b, True, y_bf16_for(d, fl)),
+           f"variant random {idx} {T},{H},{I},{E},{K}/{act}")
 
 
 def test_silu_variant_entry_equals_plain_entry():
