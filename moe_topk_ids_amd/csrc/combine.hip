@@ -20,6 +20,21 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Slot rows are read exactly once: non-temporal loads keep them from
+// displacing other lines in the L2 and last-level caches (measured on the
+// bf16 combine: wide, 537 MB of rows, 135 -> 105 us; large 91 -> 89 us).
+// Non-temporal stores of the output measured slower (+5 to +14 %) and are
+// not used.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+  typedef float f32x4_v __attribute__((ext_vector_type(4)));
+  const f32x4_v q = __builtin_nontemporal_load(reinterpret_cast<const f32x4_v*>(p));
+  return make_float4(q[0], q[1], q[2], q[3]);
+}
 // A workgroup loops over tokens t = blockIdx.x, blockIdx.x + gridDim.x, ...;
 // its lanes cover NC float4 columns each of the row's blockIdx.y-th block of
 // 256 * NC columns. Per token, the slot lookups and weights are wave-uniform
@@ -62,11 +77,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         live[j] = k0 + j < K && (slot_of ? slot_of[f] >= 0 : in);
         w[j] = topk_weights[f];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) v[j][i] = y4[f * h4 + col[i]];
+        for (int i = 0; i < NC; ++i) v[j][i] = stream_load(y4 + f * h4 + col[i]);
         for (int s = 1; s < ksplit; ++s) {  // partial sums of a split contraction, in order
 #pragma unroll
           for (int i = 0; i < NC; ++i) {
-            const float4 p = y4[s * split4 + f * h4 + col[i]];
+            const float4 p = stream_load(y4 + s * split4 + f * h4 + col[i]);
             v[j][i].x = v[j][i].x + p.x;
             v[j][i].y = v[j][i].y + p.y;
             v[j][i].z = v[j][i].z + p.z;
@@ -151,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
         ev[j] = in ? e : 0;
         w[j] = topk_weights[f];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) v[j][i] = y8[f * h8 + col[i]];
+        for (int i = 0; i < NC; ++i) v[j][i] = stream_load(y8 + f * h8 + col[i]);
       }
 #pragma unroll
       for (int j = 0; j < KP; ++j) {

@@ -21,6 +21,12 @@
 namespace moe {
 namespace {
 
+// Cache policy of the expert-weight loads: non-temporal (each weight is read
+// once per call; measured on the decode workload, 20.2 -> 19.6 us per call).
+// The per-expert streaming kernels keep default loads (non-temporal measured
+// 2 % slower there).
+constexpr int kNonTemporal = 2;  // the NT bit of the gfx950 cache-policy field
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDownIter = 32;  // 16-byte chunks per lane held in registers
@@ -72,8 +78,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup(
       const bool okr = ok && (i0 + r < I);
       const uint32_t og = okr ? (uint32_t)(((i0 + r) * H + c * 8) * 2) : kOutOfRange;
       const uint32_t ou = okr ? (uint32_t)(((I + i0 + r) * H + c * 8) * 2) : kOutOfRange;
-      wv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, og, 0, 0);
-      wv[IPW + r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ou, 0, 0);
+      wv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, og, 0, kNonTemporal);
+      wv[IPW + r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, ou, 0, kNonTemporal);
     }
     xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? (uint32_t)(c * 16) : kOutOfRange, 0, 0);
   }
@@ -140,7 +146,11 @@ __global__ __launch_bounds__(kThreads) void decode_down(
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     okj[j] = qj[j] < nq32 && ej[j] >= 0 && ej[j] < E;
-    wv[j] = w2v[okj[j] ? ((int64_t)ej[j] * H + h) * cpr + cj[j] : 0];
+    {
+      const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          &w2v[okj[j] ? ((int64_t)ej[j] * H + h) * cpr + cj[j] : 0]));
+      wv[j] = make_uint4(q[0], q[1], q[2], q[3]);
+    }
     av[j] = av_base[okj[j] ? qj[j] : 0];
   }
   float s = 0.f;
