@@ -296,6 +296,33 @@ def test_random_shapes_against_oracle(idx, path):
                  f"random {idx} {T},{H},{I},{E},{K}/{path}")
 
 
+@pytest.mark.parametrize("T,H,I,E,K", [
+    (4195, 2048, 2048, 8, 2),    # 192x256 gate/up; the down projection's column-half tail
+    (8192, 4096, 384, 128, 8),   # 256x256 at E=128
+    (135, 2048, 2048, 8, 2),     # 64x128 gate/up; contraction split of the down projection
+    (520, 4096, 384, 128, 8),    # 64-row tiles
+    (1023, 2048, 2048, 8, 2),    # 128x128
+    (2400, 2048, 768, 128, 8),   # 192-row tiles at E=128
+    (1, 2048, 768, 128, 8),      # per-token path
+    (40, 2048, 768, 128, 8),     # per-expert path
+])
+def test_repeated_calls_are_bitwise_identical(T, H, I, E, K):
+    """30 calls in a row into the same output, each compared with the first
+    bit for bit: every route is deterministic, so any difference would be a
+    race between workgroups or with the workspace."""
+    require_gpu()
+    dd = to_device(cpu_inputs(T, H, I, E, K, seed=5))
+    ref = moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                          dd["topk_ids"], flags=0).clone()
+    out = torch.empty_like(ref)
+    say(f"repeated calls T={T} H={H} I={I} E={E} K={K} path {moe.moe_path(T, H, I, E, K, 0)}")
+    for r in range(30):
+        moe.moe_forward(dd["hidden_states"], dd["w1"], dd["w2"], dd["topk_weights"],
+                        dd["topk_ids"], out=out, flags=0)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"call {r} differs"
+
+
 def test_all_tokens_one_expert_and_empty_experts():
     require_gpu()
     d = dict(cpu_inputs(700, 256, 256, 16, 2, seed=5))
