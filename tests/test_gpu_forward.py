@@ -246,6 +246,49 @@ def test_down_projection_tail_split(T, H, I, E, K):
             assert_close(a[rows], oracle_rows(d, rows), tight_rows(d, rows, f), f"tail T={T}")
 
 
+def _ids_with_counts(counts, T, K, seed):
+    """topk_ids whose expert e holds exactly counts[e] of the T*K slots, every
+    token on K distinct experts: the sorted slot list read with stride T (no
+    expert holds more than T slots), tokens shuffled."""
+    seq = np.repeat(np.arange(len(counts)), counts)
+    assert seq.size == T * K and max(counts) <= T
+    ids = seq.reshape(K, T).T
+    return ids[np.random.default_rng(seed).permutation(T)].astype(np.int32)
+
+
+@pytest.mark.parametrize("row_tiles", [44, 48, 49, 51])
+def test_down_tail_split_set_routings(row_tiles):
+    """Prefill's shape (192-row tiles, 8 column tiles of the down projection,
+    a round = 32 row tiles) with routings of set expert sizes: 44 row tiles
+    leave 3/8 of a round (halves), 48 exactly half (the halves fill one
+    round), 49 and 51 leave more than half, where the host's plan still
+    splits but the first launch runs every tile and the second finds none.
+    Same bits as the single launch on the slot and atomic paths; against the
+    oracle on 128 seeded rows."""
+    require_gpu()
+    T, H, I, E, K = 4195, 2048, 2048, 8, 2
+    fl = PATHS["slot"]
+    assert moe.moe_down_tail_split(T, H, I, E, K, fl)
+    assert moe.moe_m_tile(T, H, I, E, K) == 192
+    counts = {44: [1152] * 7 + [326],               # 7*6 + 2
+              48: [1049] * 6 + [1048] * 2,          # 8*6, balanced
+              49: [1153] + [1034] * 6 + [1033],     # 7 + 7*6
+              51: [1153] * 3 + [987] + [986] * 4}[row_tiles]  # 3*7 + 5*6
+    assert sum(counts) == T * K and sum(-(-c // 192) for c in counts) == row_tiles
+    d = dict(cpu_inputs(T, H, I, E, K, seed=T))
+    d["topk_ids"] = torch.from_numpy(_ids_with_counts(counts, T, K, seed=row_tiles))
+    dd = to_device(d)
+    rows = sample_rows(T, 128, seed=3)
+    for path, f in (("slot", fl), ("atomic", PATHS["atomic"])):
+        say(f"down tail split, {row_tiles} row tiles, {path}")
+        a = _run(dd, f)
+        b = _run(dd, f | moe.FLAG_NO_TAIL_SPLIT)
+        assert np.array_equal(a, b), path
+        if path == "slot":
+            assert_close(a[rows], oracle_rows(d, rows), tight_rows(d, rows, f),
+                         f"down tail, {row_tiles} row tiles")
+
+
 @pytest.mark.parametrize("name", ["prefill", "large"])
 def test_atomic_path_is_deterministic_for_top2(name):
     """With two routing terms per token the atomic combine is 0 + a + b in
