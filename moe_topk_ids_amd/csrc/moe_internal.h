@@ -15,9 +15,10 @@ int set_last_error(int code, const char* msg);
 // Slots handled by one routing workgroup (grows with T*K so that the number
 // of routing workgroups stays at most kRouteMaxBlocks).
 constexpr int kRouteThreads = 256;
-// Problems up to this size are routed by one workgroup in one launch.
-constexpr int64_t kRouteSingleMaxSlots = 16384;
-constexpr int64_t kRouteSingleMaxExperts = 512;
+// Problems up to this size are routed in one launch (a workgroup per 1024
+// slots).
+constexpr int64_t kRouteOnePassMaxSlots = 65536;
+constexpr int64_t kRouteOnePassMaxExperts = 512;
 constexpr int kRouteMaxBlocks = 128;
 constexpr int kMaxExperts = 1024;
 

@@ -3,10 +3,12 @@
 // kernel (kernel.py, start_a2a_scatter) fills its per-expert buffers, and
 // pads every expert's group to the GEMM row tile.
 //
-// Up to kRouteSingleMaxSlots slots (and kRouteSingleMaxExperts experts) one
-// workgroup of 16 waves does everything in a single launch (route_single):
-// every lane loads its (at most 32) ids at once, so the kernel pays one
-// memory latency, and ranking, counting and the scatter work from registers.
+// Up to kRouteOnePassMaxSlots slots (and kRouteOnePassMaxExperts experts), one
+// launch (route_onepass): workgroup g ranks slots [1024 g, 1024 g + 1024),
+// one 64-slot chunk per wave, and counts every other workgroup's slots
+// itself, so it knows its experts' starting rows without waiting for any
+// other workgroup. Every lane loads its ids (at most 16) at once: the kernel
+// pays one memory latency.
 //
 // Above that, two launches, no atomics on the ordering path:
 //   route_count    per workgroup, a per-expert histogram of its slot range
@@ -68,9 +70,29 @@ __device__ inline uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-constexpr int kSingleThreads = 1024;
-constexpr int kSingleWaves = kSingleThreads / 64;
-constexpr int kSingleChunks = (int)(kRouteSingleMaxSlots / (kSingleWaves * 64));  // per lane
+constexpr int kOnePassThreads = 1024;
+constexpr int kOnePassWaves = kOnePassThreads / 64;
+constexpr int64_t kOnePassGroupSlots = kOnePassWaves * 64;  // one 64-slot chunk per wave
+constexpr int kOnePassBatch = 16;  // workgroups' chunks loaded together for counting
+// With at most 32 experts the counts are kept in 4 copies, lane l adding to
+// copy l % 4, so that fewer lanes of one atomic instruction hit the same LDS
+// word (large, E=8: 10.5 -> 8.7 us); with more experts the lanes already
+// spread and the extra LDS to clear and sum cost 0.5-2 us.
+__host__ __device__ inline int onepass_sub(int32_t E) { return E <= 32 ? 4 : 1; }
+
+// Loads this wave's chunk of workgroups i0 .. i0+B-1 (those below G); -1 for
+// slots past the end.
+template <int B>
+__device__ __forceinline__ void onepass_load(int32_t (&v)[B], const int32_t* __restrict__ ids,
+                                             int64_t n_slots, int i0, int G, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    v[j] = -1;
+    if (i0 + j >= G) break;  // uniform
+    const int64_t f = ((int64_t)(i0 + j) * kOnePassWaves + wave) * 64 + lane;
+    if (f < n_slots) v[j] = ids[f];
+  }
+}
 
 __device__ inline void rank_and_scatter(const int32_t* __restrict__ ids, int64_t n_slots,
                                         int32_t E, int64_t wbase, int64_t per_wave,
@@ -210,124 +232,144 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   rank_and_scatter(ids, n_slots, E, wbase, per_wave, myrun, sorted, slot_of);
 }
 
-__global__ __launch_bounds__(kSingleThreads) void route_single(
+// Inclusive prefix sum over the wave: DPP row shifts inside each row of 16
+// lanes, then row broadcasts of lanes 15 and 31 into the later rows.
+__device__ __forceinline__ int32_t wave_inclusive_scan_i32(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// One launch of G = ceil(n / 1024) workgroups. Workgroup g ranks the slots
+// [1024 g, 1024 g + 1024), one 64-slot chunk per wave; it learns where its
+// slots go by counting every other workgroup's slots itself (order-free LDS
+// atomics over ids it loads from L2), so no workgroup waits for another. The
+// counting grows as G * n over the chip, which bounds n.
+__global__ __launch_bounds__(kOnePassThreads) void route_onepass(
     const int32_t* __restrict__ ids, int64_t n_slots, int32_t E, int32_t M,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
     int32_t* __restrict__ slot_of, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ num_tiles) {
-  // LDS: run[kSingleWaves][E] (per-wave counts, then each wave's first row
-  // per expert), tot[E], off[E+1]
+  // LDS: pre[E][sub] (slots of each expert before this workgroup's range),
+  // tot[E][sub] (those after it; then tot[e][0] holds the expert's total),
+  // run[kOnePassWaves][E] (each wave's count in its chunk, then where the
+  // wave's group starts inside the expert), off[E+1] (padded offsets)
   extern __shared__ int32_t lds[];
-  int32_t* run = lds;
-  int32_t* tot = run + kSingleWaves * E;
-  int32_t* off = tot + E;
+  const int sub = onepass_sub(E);
+  int32_t* pre = lds;
+  int32_t* tot = pre + sub * E;
+  int32_t* run = tot + sub * E;
+  int32_t* off = run + kOnePassWaves * E;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int g = blockIdx.x;
+  const int G = gridDim.x;
 
-  // every id of the wave's contiguous, 64-aligned slot range is loaded up
-  // front (one memory latency for the whole kernel)
-  const int64_t per_wave = ((n_slots + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
-  const int64_t wbase = (int64_t)wave * per_wave;
-  int32_t idr[kSingleChunks];
+  // the own chunk and the first batch of the others' loaded up front (one
+  // memory latency for up to 16 workgroups)
+  const int64_t own = ((int64_t)g * kOnePassWaves + wave) * 64 + lane;
+  const int32_t e = own < n_slots ? ids[own] : -1;
+  int32_t cur[kOnePassBatch], nxt[kOnePassBatch];
+  onepass_load(cur, ids, n_slots, 0, G, wave, lane);
 #pragma unroll
-  for (int c = 0; c < kSingleChunks; ++c) {
-    const int64_t f = wbase + c * 64 + lane;
-    idr[c] = (c * 64 < per_wave && f < n_slots) ? ids[f] : -1;
-  }
-  for (int i = tid; i < kSingleWaves * E; i += kSingleThreads) run[i] = 0;
+  for (int j = 0; j < kOnePassBatch; ++j) nxt[j] = -1;
+  for (int i = tid; i < (2 * sub + kOnePassWaves) * E; i += kOnePassThreads) lds[i] = 0;
   __syncthreads();
 
-  // 1. rank each chunk by ballot (lowest lane first among equal ids); the
-  //    group's first lane bumps the wave's count of that expert, and the
-  //    value it read is the group's start inside the wave
+  // 1. the other workgroups' slots, counted before / after this range; the
+  //    next batch loads while this one is counted
+  for (int i0 = 0; i0 < G; i0 += kOnePassBatch) {
+    if (i0 + kOnePassBatch < G) onepass_load(nxt, ids, n_slots, i0 + kOnePassBatch, G, wave, lane);
+#pragma unroll
+    for (int j = 0; j < kOnePassBatch; ++j) {
+      const int i = i0 + j;
+      if (i >= G) break;  // uniform
+      const int32_t x = cur[j];
+      if (i != g && x >= 0 && x < E)
+        atomicAdd((i < g ? pre : tot) + x * sub + (lane & (sub - 1)), 1);
+    }
+#pragma unroll
+    for (int j = 0; j < kOnePassBatch; ++j) cur[j] = nxt[j];
+  }
+  // 2. the own chunk ranked by ballot (lowest lane first among equal ids);
+  //    the group's first lane records the wave's count of that expert
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  int32_t* myrun = run + wave * E;
-#pragma unroll
-  for (int c = 0; c < kSingleChunks; ++c) {
-    if (c * 64 >= per_wave) break;  // uniform
-    const int32_t e = idr[c];
-    const bool valid = e >= 0 && e < E;
-    uint64_t mask = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((e >> bit) & 1);
-      const uint64_t bm = __ballot(set);
-      mask &= set ? bm : ~bm;
-    }
-    const int32_t rank = __popcll(mask & lanemask_lt());
-    int32_t start = 0;
-    if (valid && rank == 0) start = atomicAdd(&myrun[e], __popcll(mask));
-    const int leader = valid ? __ffsll((long long)mask) - 1 : lane;
-    start = __shfl(start, leader, 64);
-    // keep (place in the wave, expert) in the id's register: place < 2048,
-    // expert < 512
-    idr[c] = valid ? ((start + rank) << 11) | e : -1;
+  const bool valid = e >= 0 && e < E;
+  uint64_t mask = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = valid && ((e >> bit) & 1);
+    const uint64_t bm = __ballot(set);
+    mask &= set ? bm : ~bm;
   }
+  const int32_t rank = __popcll(mask & lanemask_lt());
+  if (valid && rank == 0) run[wave * E + e] = __popcll(mask);
   __syncthreads();
 
-  // 2. and 3. in wave 0: per expert the total and each wave's exclusive
-  //    prefix inside the expert (the 16 per-wave counts read together), then
-  //    an exclusive scan of the padded counts over experts with shuffles;
-  //    lane l owns experts l*EPL .. l*EPL+EPL-1
+  // 3. in wave 0: per expert the waves' starts (after the earlier
+  //    workgroups' slots) and the total, then an exclusive scan of the padded
+  //    totals over experts; lane l owns experts l*EPL .. l*EPL+EPL-1
   if (wave == 0) {
     const int epl = (E + 63) / 64;
     int32_t lane_sum = 0;
     for (int q = 0; q < epl; ++q) {
-      const int e = lane * epl + q;
-      if (e >= E) break;
-      int32_t cw[kSingleWaves];
+      const int x = lane * epl + q;
+      if (x >= E) break;
+      int32_t cw[kOnePassWaves];
 #pragma unroll
-      for (int w = 0; w < kSingleWaves; ++w) cw[w] = run[w * E + e];
-      int32_t a = 0;
+      for (int w = 0; w < kOnePassWaves; ++w) cw[w] = run[w * E + x];
+      int32_t a = 0, after = 0;
+      for (int c = 0; c < sub; ++c) {
+        a += pre[x * sub + c];
+        after += tot[x * sub + c];
+      }
 #pragma unroll
-      for (int w = 0; w < kSingleWaves; ++w) {
-        run[w * E + e] = a;
+      for (int w = 0; w < kOnePassWaves; ++w) {
+        run[w * E + x] = a;
         a += cw[w];
       }
-      tot[e] = a;
+      a += after;
+      tot[x * sub] = a;
       lane_sum += (a + M - 1) / M * M;
     }
-    int32_t incl = lane_sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
-    }
+    const int32_t incl = wave_inclusive_scan_i32(lane_sum);
     int32_t acc = incl - lane_sum;
     for (int q = 0; q < epl; ++q) {
-      const int e = lane * epl + q;
-      if (e >= E) break;
-      off[e] = acc;
-      acc += (tot[e] + M - 1) / M * M;
+      const int x = lane * epl + q;
+      if (x >= E) break;
+      off[x] = acc;
+      acc += (tot[x * sub] + M - 1) / M * M;
     }
     if (lane == 63) off[E] = incl;
   }
   __syncthreads();
 
-  // 4. metadata, pad rows, tile->expert map
-  for (int e = tid; e < E; e += kSingleThreads) counts[e] = tot[e];
-  for (int e = tid; e <= E; e += kSingleThreads) offsets[e] = off[e];
-  if (tid == 0) num_tiles[0] = off[E] / M;
-  for (int e = wave; e < E; e += kSingleWaves) {
-    const int32_t start = off[e], padded = off[e + 1] - off[e];
-    for (int32_t j = lane; j < padded / M; j += 64) tile_expert[start / M + j] = (int32_t)e;
-    for (int32_t r = tot[e] + lane; r < padded; r += 64) sorted[start + r] = -1;
+  // 4. metadata from workgroup 0; pad rows and the tile->expert map of
+  //    expert x from workgroup x % G
+  if (g == 0) {
+    for (int x = tid; x < E; x += kOnePassThreads) counts[x] = tot[x * sub];
+    for (int x = tid; x <= E; x += kOnePassThreads) offsets[x] = off[x];
+    if (tid == 0) num_tiles[0] = off[E] / M;
+  }
+  for (int x = g + G * wave; x < E; x += G * kOnePassWaves) {
+    const int32_t start = off[x], padded = off[x + 1] - off[x];
+    for (int32_t j = lane; j < padded / M; j += 64) tile_expert[start / M + j] = (int32_t)x;
+    for (int32_t r = tot[x * sub] + lane; r < padded; r += 64) sorted[start + r] = -1;
   }
 
-  // 5. scatter: row = expert start + earlier waves' count + place in the wave
-#pragma unroll
-  for (int c = 0; c < kSingleChunks; ++c) {
-    if (c * 64 >= per_wave) break;  // uniform
-    const int64_t f = wbase + c * 64 + lane;
-    const bool in = f < n_slots;
-    const int32_t v = idr[c];
-    if (in && v >= 0) {
-      const int32_t e = v & 0x7ff;
-      const int32_t pos = off[e] + run[wave * E + e] + (v >> 11);
+  // 5. scatter: row = expert start + the wave's start + place in the chunk
+  const int64_t f = ((int64_t)g * kOnePassWaves + wave) * 64 + lane;
+  if (f < n_slots) {
+    if (valid) {
+      const int32_t pos = off[e] + run[wave * E + e] + rank;
       sorted[pos] = (int32_t)f;
       slot_of[f] = pos;
-    } else if (in) {
+    } else {
       slot_of[f] = -1;
     }
   }
@@ -360,9 +402,11 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int
                         int32_t* tile_expert, int32_t* num_tiles, hipStream_t stream) {
   const int64_t n = T * K;
   if (n == 0) return hipSuccess;
-  if (n <= kRouteSingleMaxSlots && E <= kRouteSingleMaxExperts) {
-    const size_t lds = (size_t)(kSingleWaves * E + E + E + 1) * sizeof(int32_t);
-    route_single<<<dim3(1), dim3(kSingleThreads), lds, stream>>>(
+  if (n <= kRouteOnePassMaxSlots && E <= kRouteOnePassMaxExperts) {
+    const size_t lds =
+        (size_t)((2 * onepass_sub((int32_t)E) + kOnePassWaves) * E + E + 1) * sizeof(int32_t);
+    const int groups = (int)((n + kOnePassGroupSlots - 1) / kOnePassGroupSlots);
+    route_onepass<<<dim3(groups), dim3(kOnePassThreads), lds, stream>>>(
         ids, n, (int32_t)E, m_tile, counts, offsets, sorted, slot_of, tile_expert, num_tiles);
     return hipGetLastError();
   }
