@@ -88,8 +88,9 @@ struct SbArgs {
   Epilogue ep;  // activation variant and gate/up bias (b2 is the combine's)
 };
 
-// NC: 16-byte chunks per lane per gate/up row (H / 512 rounded up).
-template <int NC>
+// NC: 16-byte chunks per lane per gate/up row (H / 512 rounded up). WIDE:
+// the batch averages 8+ slots per expert.
+template <int NC, bool WIDE>
 __global__ __launch_bounds__(kThreads) void sb_gateup(SbArgs a) {
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ int32_t s_slots[kSmallBatchMaxSlots];
@@ -113,8 +114,11 @@ __global__ __launch_bounds__(kThreads) void sb_gateup(SbArgs a) {
     uv[j] = __builtin_amdgcn_raw_buffer_load_b128(
         wr, ok ? (uint32_t)(((I + i) * H + c * 8) * 2) : kOutOfRange, 0, 0);
   }
-  // token rows of SB slots are loaded together, so their latency overlaps
-  constexpr int SB = NC <= 2 ? 4 : (NC <= 4 ? 2 : 1);
+  // token rows of SB slots are loaded together, so their latency overlaps;
+  // with many slots per expert up to 16 chunks per lane, so that a batch pays
+  // about one L2 round trip for its rows (with one or two, the extra rows
+  // would be repeats)
+  constexpr int SB = WIDE ? (NC >= 16 ? 1 : 16 / NC) : (NC <= 2 ? 4 : (NC <= 4 ? 2 : 1));
   const int32_t count = s_count;
   for (int32_t m0 = 0; m0 < count; m0 += SB) {
     u32x4_t xv[SB][NC];
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void sb_gateup(SbArgs a) {
 }
 
 // G lanes per w2 row, R = 64 / G rows per wave, JD chunks per lane per row
-// (G * JD >= I / 8).
-template <int G, int JD>
+// (G * JD >= I / 8); WIDE as for sb_gateup.
+template <int G, int JD, bool WIDE>
 __global__ __launch_bounds__(kThreads) void sb_down(SbArgs a) {
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ int32_t s_slots[kSmallBatchMaxSlots];
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(kThreads) void sb_down(SbArgs a) {
     wv[j] = __builtin_amdgcn_raw_buffer_load_b128(
         wr, (h_ok && c < cpr) ? (uint32_t)((h * I + c * 8) * 2) : kOutOfRange, 0, 0);
   }
-  constexpr int SB = JD <= 8 ? 2 : 1;  // activation rows loaded together
+  // activation rows loaded together
+  constexpr int SB = WIDE ? (JD >= 16 ? 1 : 16 / JD) : (JD <= 8 ? 2 : 1);
   const int32_t count = s_count;
   for (int32_t m0 = 0; m0 < count; m0 += SB) {
     u32x4_t av[SB][JD];
@@ -221,17 +226,40 @@ __global__ __launch_bounds__(kThreads) void sb_down(SbArgs a) {
   }
 }
 
-template <int G>
+template <int G, bool WIDE>
 hipError_t launch_down_g(const SbArgs& a, int64_t jd, int64_t rows_per_block, unsigned gy,
                          hipStream_t stream) {
   const dim3 grid((unsigned)((a.H + rows_per_block - 1) / rows_per_block), gy);
-  if (jd <= 2) sb_down<G, 2><<<grid, kThreads, 0, stream>>>(a);
-  else if (jd <= 4) sb_down<G, 4><<<grid, kThreads, 0, stream>>>(a);
-  else if (jd <= 6) sb_down<G, 6><<<grid, kThreads, 0, stream>>>(a);
-  else if (jd <= 8) sb_down<G, 8><<<grid, kThreads, 0, stream>>>(a);
-  else if (jd <= 16) sb_down<G, 16><<<grid, kThreads, 0, stream>>>(a);
-  else sb_down<G, 32><<<grid, kThreads, 0, stream>>>(a);
+  if (jd <= 2) sb_down<G, 2, WIDE><<<grid, kThreads, 0, stream>>>(a);
+  else if (jd <= 4) sb_down<G, 4, WIDE><<<grid, kThreads, 0, stream>>>(a);
+  else if (jd <= 6) sb_down<G, 6, WIDE><<<grid, kThreads, 0, stream>>>(a);
+  else if (jd <= 8) sb_down<G, 8, WIDE><<<grid, kThreads, 0, stream>>>(a);
+  else if (jd <= 16) sb_down<G, 16, WIDE><<<grid, kThreads, 0, stream>>>(a);
+  else sb_down<G, 32, WIDE><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool WIDE>
+hipError_t launch_down(const SbArgs& a, int64_t g, int64_t jd, int64_t rows_per_block,
+                       unsigned gy, hipStream_t stream) {
+  switch (g) {
+    case 1: return launch_down_g<1, WIDE>(a, jd, rows_per_block, gy, stream);
+    case 2: return launch_down_g<2, WIDE>(a, jd, rows_per_block, gy, stream);
+    case 4: return launch_down_g<4, WIDE>(a, jd, rows_per_block, gy, stream);
+    case 8: return launch_down_g<8, WIDE>(a, jd, rows_per_block, gy, stream);
+    case 16: return launch_down_g<16, WIDE>(a, jd, rows_per_block, gy, stream);
+    case 32: return launch_down_g<32, WIDE>(a, jd, rows_per_block, gy, stream);
+    default: return launch_down_g<64, WIDE>(a, jd, rows_per_block, gy, stream);
+  }
+}
+
+template <bool WIDE>
+void launch_gateup(const SbArgs& a, int64_t nc, dim3 g1, hipStream_t stream) {
+  if (nc <= 1) sb_gateup<1, WIDE><<<g1, kThreads, 0, stream>>>(a);
+  else if (nc <= 2) sb_gateup<2, WIDE><<<g1, kThreads, 0, stream>>>(a);
+  else if (nc <= 4) sb_gateup<4, WIDE><<<g1, kThreads, 0, stream>>>(a);
+  else if (nc <= 8) sb_gateup<8, WIDE><<<g1, kThreads, 0, stream>>>(a);
+  else sb_gateup<16, WIDE><<<g1, kThreads, 0, stream>>>(a);
 }
 
 }  // namespace
@@ -263,29 +291,27 @@ hipError_t launch_small_batch(const uint16_t* hidden, const uint16_t* w1, const 
   const unsigned gy = (unsigned)(a.n < E ? a.n : E);
   const int64_t nc = (H / 8 + 63) / 64;
   const dim3 g1((unsigned)((I + kWaves - 1) / kWaves), gy);
-  if (nc <= 1) sb_gateup<1><<<g1, kThreads, 0, stream>>>(a);
-  else if (nc <= 2) sb_gateup<2><<<g1, kThreads, 0, stream>>>(a);
-  else if (nc <= 4) sb_gateup<4><<<g1, kThreads, 0, stream>>>(a);
-  else if (nc <= 8) sb_gateup<8><<<g1, kThreads, 0, stream>>>(a);
-  else sb_gateup<16><<<g1, kThreads, 0, stream>>>(a);
+  // 8+ slots per present expert on average and small experts (H*I <= 2^20,
+  // where the call is latency-bound): load more slot rows at once. T=64,
+  // H=512, I=256, E=8, top-2: 32.1 -> 27.2 us per call. On every batch the
+  // same widening measured 5-65 % slower at H=2048 (E=8 and E=128: each wave
+  // re-reads more activation rows from L2), and 1-3 % faster at H=I=4096.
+  const bool wide = a.n >= 8 * (int64_t)gy && H * I <= (int64_t)1 << 20;
+  if (wide) launch_gateup<true>(a, nc, g1, stream);
+  else launch_gateup<false>(a, nc, g1, stream);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   // lanes per w2 row: the smallest power of two giving at most 8 chunks per
-  // lane (at most 32 once all 64 lanes share one row)
+  // lane (2 for a wide batch, so that a wave loads 8 slots' activation rows
+  // at once; more once all 64 lanes share one row)
   const int64_t cpr = I / 8;
+  const int64_t per_lane = wide ? 2 : 8;
   int64_t g = 1;
-  while (g < 64 && g * 8 < cpr) g *= 2;
+  while (g < 64 && g * per_lane < cpr) g *= 2;
   const int64_t jd = (cpr + g - 1) / g;
   const int64_t rows_per_block = kWaves * (64 / g);
-  switch (g) {
-    case 1: return launch_down_g<1>(a, jd, rows_per_block, gy, stream);
-    case 2: return launch_down_g<2>(a, jd, rows_per_block, gy, stream);
-    case 4: return launch_down_g<4>(a, jd, rows_per_block, gy, stream);
-    case 8: return launch_down_g<8>(a, jd, rows_per_block, gy, stream);
-    case 16: return launch_down_g<16>(a, jd, rows_per_block, gy, stream);
-    case 32: return launch_down_g<32>(a, jd, rows_per_block, gy, stream);
-    default: return launch_down_g<64>(a, jd, rows_per_block, gy, stream);
-  }
+  return wide ? launch_down<true>(a, g, jd, rows_per_block, gy, stream)
+              : launch_down<false>(a, g, jd, rows_per_block, gy, stream);
 }
 
 }  // namespace moe
