@@ -164,6 +164,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier of a ring deeper than two stages: this wave's LDS reads
+// complete, then the barrier, with no fence (a fence would make the compiler
+// wait for every outstanding load, the later stages' included). The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Epilogue of one wave's WTM x WTN sub-tile (wave position wm, wn in the
 // tile): lane holds, for token row (lane & 31) of sub-tile tm, the weight
 // columns 8*j + 4*(lane >> 5) + {0,1,2,3} of sub-tile tn, in
@@ -647,7 +658,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 
     constexpr int KK = BK / 16;  // matrix-core sub-steps per stage (even)
     static_assert(KK % 2 == 0, "fragment double buffer alternates per sub-step");
-    static_assert(NS == 2, "two-stage ring");
+    static_assert(NS == 2 || NS == 4, "two- or four-stage ring");
+    static_assert(!Q || NS == 2, "fp8 weights: two-stage ring");
     // Matrix ops of a stage's last sub-step issued ahead of the stage
     // boundary: a quarter of them in the bf16 gate/up product with 256-row
     // tiles (measured 3-4 % faster there); elsewhere none (equal or slower).
@@ -682,37 +694,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
       }                                                                                          \
     } while (0)
 
-    // prologue: stages 0 and 1 in flight (one per buffer; a missing stage 1
-    // reads out of range), stage 0 landed, its first fragments read
-    MOE_ISSUE_STAGE(0, 0);
-    MOE_ISSUE_STAGE(1, 1);
-    wait_vmcnt<LA + LB>();
-    __syncthreads();
+    // prologue: stages 0 .. NS-1 in flight (one per buffer; missing stages
+    // read out of range), stage 0 landed, its first fragments read
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) MOE_ISSUE_STAGE(s0, s0);
+    wait_vmcnt<(NS - 1) * (LA + LB)>();
+    if constexpr (NS == 2) __syncthreads();
+    else ring_barrier();
     bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
     MOE_LOAD_FRAGS(f0, 0, 0, 0);
     MOE_WIDEN(f0, 0);
 
     // Every stage but the last. Its last sub-step's fragments are already in
     // registers, so the stage boundary is interleaved with that sub-step's
-    // matrix ops: the first PRE of them, then the wait (stage kt+1 landed: it
-    // is the only stage in flight) and the barrier (every wave is done reading
-    // stage kt), then the loads of stage kt+2 into the buffer stage kt leaves
-    // (issued first: they have the longest way to go), the reads of stage
-    // kt+1's first fragments, then the rest of the matrix ops. The last stage
-    // is peeled off, so the loop body has no branch (with one, the
-    // accumulators are copied between register files around it).
+    // matrix ops: the first PRE of them, then the wait (stage kt+1 landed;
+    // with four buffers stages kt+2 and kt+3 stay in flight) and the barrier
+    // (every wave is done reading stage kt), then the loads of stage kt+NS
+    // into the buffer stage kt leaves (issued first: they have the longest way
+    // to go), the reads of stage kt+1's first fragments, then the rest of the
+    // matrix ops. The last stage is peeled off, so the loop body has no branch
+    // (with one, the accumulators are copied between register files around
+    // it).
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      const int buf = kt & 1;
+      const int buf = kt & (NS - 1);
       MOE_SUBSTEPS(buf, kt);
       MOE_MMA(f1, 0, PRE);
-      wait_vmcnt<0>();
-      __syncthreads();
-      MOE_ISSUE_STAGE(buf, kt + 2);
-      MOE_LOAD_FRAGS(f0, buf ^ 1, 0, kt + 1);
+      if constexpr (NS == 2) {
+        wait_vmcnt<0>();
+        __syncthreads();
+      } else {
+        wait_vmcnt<(NS - 2) * (LA + LB)>();
+        ring_barrier();
+      }
+      MOE_ISSUE_STAGE(buf, kt + NS);
+      MOE_LOAD_FRAGS(f0, (kt + 1) & (NS - 1), 0, kt + 1);
       MOE_MMA(f1, PRE, TM * TN - PRE);
       MOE_WIDEN(f0, 0);
     }
-    MOE_SUBSTEPS((nk - 1) & 1, nk - 1);
+    MOE_SUBSTEPS((nk - 1) & (NS - 1), nk - 1);
     MOE_MMA(f1, 0, TM * TN);
 #undef MOE_SUBSTEPS
 #undef MOE_MMA
@@ -760,6 +779,15 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   a.group_m = 8;
   // (token rows, weight rows, waves): the variants kept after sweeping tile
   // shape, pipeline depth and wave layout on the workloads' shapes
+  if constexpr (!Q) {
+    // four-stage rings for launches of at most one tile per CU (a stage's
+    // latency is then not covered by other workgroups' work)
+    if (cfg.ns == 4) {
+      if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 4, MODE, Q>(a, stream);
+      if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 64, 2, 2, 4, MODE, Q>(a, stream);
+      if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 4, MODE, Q>(a, stream);
+    }
+  }
   if (cfg.bm == 64 && cfg.bn == 256) return launch_cfg<64, 256, 64, 1, 4, 2, MODE, Q>(a, stream);
   if (cfg.bm == 64 && cfg.bn == 128) return launch_cfg<64, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
   if (cfg.bm == 128 && cfg.bn == 128) return launch_cfg<128, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
@@ -843,6 +871,16 @@ double model_cost(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E, GemmCfg
 }
 }  // namespace
 
+// A four-stage ring where a launch expects at most one tile per CU: with no
+// other workgroup's work to cover a stage's latency, each tile then keeps
+// three stages in flight instead of one. For the 64- and 128-row tiles,
+// whose four stages fit a CU's LDS.
+int pick_ring_stages(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles) {
+  const bool fits =
+      (cfg.bm == 64 && (cfg.bn == 128 || cfg.bn == 256)) || (cfg.bm == 128 && cfg.bn == 128);
+  return fits && expected_row_tiles(T, K, E, cfg.bm) * (double)n_tiles <= 256.0 ? 4 : 2;
+}
+
 GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
   const GemmCfg cands[5] = {{64, 128}, {64, 256}, {128, 128}, {192, 256}, {256, 256}};
   GemmCfg best = cands[2];
@@ -859,6 +897,7 @@ GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E) {
       best_t = t;
     }
   }
+  best.ns = pick_ring_stages(best, T, K, E, I / (best.bn / 2));
   return best;
 }
 

@@ -243,6 +243,7 @@ Layout make_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32
               : moe::pick_ksplit(L.g2, T, K, E, (H + L.g2.bn - 1) / L.g2.bn, I);
   L.y16 = y_bf16_choice(L.ks2, flags);
   if (L.y16) L.ks2 = 1;  // bf16 rows are whole sums, rounded once
+  L.g2.ns = moe::pick_ring_stages(L.g2, T, K, E, (H + L.g2.bn - 1) / L.g2.bn * L.ks2);
   L.cap = moe::padded_capacity(n, E, L.g1.bm);
   L.max_tiles = L.cap / L.g1.bm;
   L.tail = L.ks2 == 1 && !(flags & (MOE_FLAG_NO_TAIL_SPLIT | MOE_FLAG_FP8_WEIGHTS)) &&

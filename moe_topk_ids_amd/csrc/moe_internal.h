@@ -49,11 +49,15 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int
 // Every grouped GEMM skips a row tile whose tile_expert entry is outside
 // [0, E) rather than address weights past the end of w1/w2.
 struct GemmCfg {
-  int bm;  // token rows per tile (the routing m_tile)
-  int bn;  // weight rows per tile (GEMM1: half gate, half up)
+  int bm;      // token rows per tile (the routing m_tile)
+  int bn;      // weight rows per tile (GEMM1: half gate, half up)
+  int ns = 2;  // stages of the global->LDS ring (pick_ring_stages)
 };
 
 GemmCfg pick_gemm1_cfg(int64_t T, int64_t K, int64_t H, int64_t I, int64_t E);
+// 4 (a four-stage ring) where a launch of n_tiles column tiles per row tile
+// expects at most one tile per CU and the tile's stages fit, else 2.
+int pick_ring_stages(GemmCfg cfg, int64_t T, int64_t K, int64_t E, int64_t n_tiles);
 GemmCfg pick_gemm2_cfg(int64_t n_slots, int64_t H, int64_t I, int64_t E, int bm);
 
 // FP8-weight grouped GEMMs: the weight tiles are staged as codes and widened
