@@ -795,7 +795,10 @@ hipError_t dispatch(GemmCfg cfg, GemmArgs a, hipStream_t stream) {
   if (cfg.bm == 256 && cfg.bn == 256) return launch_cfg<256, 256, 64, 2, 4, 2, MODE, Q>(a, stream);
   if constexpr (MODE != kGateUpSilu && !Q) {
     // column halves of the down projection's tail: the 192x256 and 256x256
-    // tiles' per-wave shapes on four waves
+    // tiles' per-wave shapes on four waves (one workgroup per CU; the
+    // 192-row halves hold a four-stage ring in the CU's 160 KB of LDS)
+    if (cfg.ns == 4 && cfg.bm == 192 && cfg.bn == 128)
+      return launch_cfg<192, 128, 64, 2, 2, 4, MODE, Q>(a, stream);
     if (cfg.bm == 192 && cfg.bn == 128) return launch_cfg<192, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
     if (cfg.bm == 256 && cfg.bn == 128) return launch_cfg<256, 128, 64, 2, 2, 2, MODE, Q>(a, stream);
   }
@@ -1039,7 +1042,9 @@ hipError_t launch_gemm2(GemmCfg cfg, const uint16_t* act, const uint16_t* w2,
   if (st != hipSuccess) return st;
   a.phase = 2;
   a.n_tiles = (int)(H / 128);
-  return run(GemmCfg{cfg.bm, 128}, a);
+  GemmCfg half{cfg.bm, 128};
+  half.ns = cfg.bm == 192 ? 4 : 2;  // 4 x 40 KB stages fill the LDS; 256-row stages do not fit
+  return run(half, a);
 }
 
 bool fp8_gemm_supported(int64_t H, int64_t I, int64_t block) {
