@@ -44,12 +44,18 @@ int hip_error(const char* what, hipError_t st) {
 //  - the per-expert small-batch path streams each routed expert once, like
 //    the grouped path, but spends about 1.4e-7 us per T*K*H*I on its vector
 //    dot products; it wins until that reaches the grouped path's extra cost
-//    over streaming the weights (routing, sparse tiles, the fp32 slot
-//    buffer), measured as about 60 us + 0.06 us per MB of routed weights;
+//    over streaming the weights (routing, sparse tiles, the slot rows):
+//    about 24 us + 0.065 us per MB of routed weights with bf16 weights (the
+//    sweep repeated on the current kernels put the crossovers at T ~ 28 for
+//    2048/2048/8/2, ~ 56 for 2048/768/128/8, ~ 40 for 4096/384/128/8 and
+//    ~ 20 for 4096/4096/8/2), and 60 us + 0.06 us per MB as first fitted
+//    with FP8 weights, where the grouped path adds its widening cost;
 //  - the grouped MFMA path beyond.
 constexpr double kSmallBatchUsPerWork = 1.4e-7;
-constexpr double kGroupedFixedUs = 60.0;
-constexpr double kGroupedUsPerWeightMB = 0.06;
+constexpr double kGroupedFixedUs = 24.0;
+constexpr double kGroupedUsPerWeightMB = 0.065;
+constexpr double kGroupedFixedUsFp8 = 60.0;
+constexpr double kGroupedUsPerWeightMBFp8 = 0.06;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -149,7 +155,10 @@ int pick_path(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, uint32_t fl
            : fp8_native_for_every_block(H, I)
                  ? std::min(fp8_widen_us(H, I, E), fp8_in_register_us(T, H, I, E, K))
                  : fp8_widen_us(H, I, E);
-  if (sb && sb_extra_us <= kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb + dequant_us)
+  const double grouped_extra_us =
+      fp8 ? kGroupedFixedUsFp8 + kGroupedUsPerWeightMBFp8 * routed_mb + dequant_us
+          : kGroupedFixedUs + kGroupedUsPerWeightMB * routed_mb;
+  if (sb && sb_extra_us <= grouped_extra_us)
     return MOE_PATH_SMALL_BATCH;
   return MOE_PATH_GROUPED;
 }
