@@ -190,6 +190,15 @@ def test_path_choice(lib):
     assert moe.moe_path(2, 2048, 2048, 8, 2) == moe.PATH_DECODE
     assert moe.moe_path(16, 2048, 2048, 8, 2) == moe.PATH_SMALL_BATCH
     assert moe.moe_path(135, 2048, 2048, 8, 2) == moe.PATH_GROUPED
+    # the small-batch / grouped crossovers of the sweep the path model was fitted to
+    # (each side the faster path measured there)
+    assert moe.moe_path(24, 2048, 2048, 8, 2) == moe.PATH_SMALL_BATCH
+    assert moe.moe_path(32, 2048, 2048, 8, 2) == moe.PATH_GROUPED
+    assert moe.moe_path(48, 2048, 768, 128, 8) == moe.PATH_SMALL_BATCH
+    assert moe.moe_path(64, 2048, 768, 128, 8) == moe.PATH_GROUPED
+    assert moe.moe_path(64, 4096, 384, 128, 8) == moe.PATH_GROUPED
+    assert moe.moe_path(16, 4096, 4096, 8, 2) == moe.PATH_SMALL_BATCH
+    assert moe.moe_path(24, 4096, 4096, 8, 2) == moe.PATH_GROUPED
     assert moe.moe_uses_decode_path(8, 2048, 768, 128, 8)
     assert not moe.moe_uses_decode_path(32, 2048, 768, 128, 8)
     # the small-batch workspace holds the bf16 activations and fp32 slot rows
