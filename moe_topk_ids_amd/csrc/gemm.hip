@@ -446,6 +446,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
   // stores drain, instead of after the workgroup slot is freed and
   // dispatched again. The barrier at the top keeps the previous tile's last
   // LDS reads ahead of the next tile's loads.
+  // the routing's live row tiles: fixed for the launch, read once
+  const int live_m = min(args.num_tiles[0], args.max_tiles);
   for (int vb = blockIdx.x; vb < args.nvb; vb += gridDim.x) {
     __syncthreads();
 
@@ -460,7 +462,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
     // evenly over the XCDs. Only the routing's live row tiles are numbered,
     // so the rounds are the live tiles' rounds.
     const int n_tiles = args.n_tiles;
-    const int live_m = min(args.num_tiles[0], args.max_tiles);
     // the tile order: live_m row tiles x n_ord column tiles (in phase 2 the
     // phase-1 launch's, twice this launch's width); phase 1 keeps its whole
     // rounds when the rest fills at most half a round, phase 2 takes that rest
@@ -699,8 +700,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm(GemmArgs args) {
 #pragma unroll
     for (int s0 = 0; s0 < NS; ++s0) MOE_ISSUE_STAGE(s0, s0);
     wait_vmcnt<(NS - 1) * (LA + LB)>();
-    if constexpr (NS == 2) __syncthreads();
-    else ring_barrier();
+    ring_barrier();  // no fence: the later stages stay in flight
     bf16x8_t f0a[TN], f0b[TM], f1a[TN], f1b[TM];
     MOE_LOAD_FRAGS(f0, 0, 0, 0);
     MOE_WIDEN(f0, 0);
